@@ -1,0 +1,159 @@
+"""Seeded synthetic workloads for exact attention.
+
+This module only draws random inputs and describes shapes. It holds none of
+the attention arithmetic, so both the HIP path and the fp64 oracle can be fed
+from it without sharing any computation.
+
+Recipe (applies to every workload):
+  * one ``torch.Generator`` on the CPU, seeded (default seed 0);
+  * fp32 standard-normal draws in the order Q, K, V, then dO (only for
+    workloads with a backward pass), each of shape [B, H, N, d];
+  * then the per-workload extras, in this order: the key-padding lengths
+    (``randint(lo, hi + 1, (B,))``), then the outlier key rows (for each
+    (b, h) in row-major order, ``randperm(N)[:round(frac * N)]`` and those K
+    rows multiplied by the factor);
+  * finally a round-to-nearest-even cast of Q, K, V, dO to the workload dtype.
+
+The workloads are named after the shapes the pages discuss: BERT-large at
+sequence 512 and GPT-2 at 1K (the end-to-end results quoted on the Ultralytics
+glossary page, section "Impatto sull'addestramento e sui contesti lunghi"), the
+32-head 4096-token example of the onecalc.app attention-memory calculator
+(section "計算例"), and the 23,400-step, 12-head trading day of the
+marketmaker.cc article (its opening section). Standard-normal synthetic data
+stands in for every dataset; no real model, weight or text is used.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Dict, Optional, Tuple
+
+import torch
+
+DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+ELEM_BYTES = {"fp32": 4, "fp16": 2, "bf16": 2}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool = False
+    kv_len_range: Optional[Tuple[int, int]] = None  # inclusive (lo, hi)
+    k_outlier_frac: float = 0.0
+    k_outlier_scale: float = 1.0
+    backward: bool = False
+    measurement_only: bool = False
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def elem_bytes(self) -> int:
+        return ELEM_BYTES[self.dtype]
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+TINY = Workload("tiny_fp32_fwd", 1, 1, 256, 64, "fp32",
+                note="B=1 H=1 N=256 d=64 fp32, no mask")
+BERT = Workload("bert_large_fp16_fwd", 32, 16, 512, 64, "fp16",
+                kv_len_range=(128, 512),
+                note="B=32 H=16 N=512 d=64 fp16, key padding U[128,512]")
+LONG = Workload("long_context_bf16_fwd", 1, 32, 4096, 128, "bf16",
+                k_outlier_frac=0.01, k_outlier_scale=8.0,
+                note="B=1 H=32 N=4096 d=128 bf16, 1% of K rows x8")
+TRADE = Workload("trading_day_bf16_causal_fwd", 1, 12, 23400, 64, "bf16",
+                 causal=True,
+                 note="B=1 H=12 N=23400 d=64 bf16 causal")
+GPT2 = Workload("gpt2_bf16_causal_fwd_bwd", 8, 12, 1024, 64, "bf16",
+                causal=True, backward=True,
+                note="B=8 H=12 N=1024 d=64 bf16 causal, forward + backward")
+
+# Backward at N >= 4096: the same generator on the long-context and
+# trading-day shapes, used for timing the backward at long sequence length.
+LONG_BWD = LONG.with_(name="long_context_bf16_bwd", backward=True,
+                      measurement_only=True)
+TRADE_BWD = TRADE.with_(name="trading_day_bf16_causal_bwd", backward=True,
+                        measurement_only=True)
+
+CONFIGS: Dict[str, Workload] = {w.name: w for w in (TINY, BERT, LONG, TRADE, GPT2)}
+MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD)}
+ALL: Dict[str, Workload] = {**CONFIGS, **MEASUREMENT}
+
+
+def make_inputs(w: Workload, seed: int = 0) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw the seeded inputs of ``w`` on the CPU, already cast to its dtype.
+
+    Returns a dict with ``q, k, v`` (and ``do`` when ``w.backward``) as
+    contiguous [B, H, N, d] tensors and ``kv_len`` as an int32 [B] tensor or
+    ``None``. The same seed always yields bit-identical tensors.
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    do = torch.randn(shape, generator=g, dtype=torch.float32) if w.backward else None
+    kv_len = None
+    if w.kv_len_range is not None:
+        lo, hi = w.kv_len_range
+        kv_len = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64)
+        kv_len = kv_len.to(torch.int32)
+    if w.k_outlier_frac > 0.0:
+        count = int(round(w.k_outlier_frac * w.N))
+        for b in range(w.B):
+            for h in range(w.H):
+                idx = torch.randperm(w.N, generator=g)[:count]
+                k[b, h, idx] *= w.k_outlier_scale
+    dt = w.torch_dtype
+    out = {
+        "q": q.to(dt).contiguous(),
+        "k": k.to(dt).contiguous(),
+        "v": v.to(dt).contiguous(),
+        "do": do.to(dt).contiguous() if do is not None else None,
+        "kv_len": kv_len,
+    }
+    return out
+
+
+def outlier_rows(w: Workload, seed: int = 0) -> Optional[torch.Tensor]:
+    """The [B, H, count] indices of the scaled K rows drawn by ``make_inputs``."""
+    if w.k_outlier_frac <= 0.0:
+        return None
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    shape = (w.B, w.H, w.N, w.d)
+    for _ in range(4 if w.backward else 3):
+        torch.randn(shape, generator=g, dtype=torch.float32)
+    if w.kv_len_range is not None:
+        lo, hi = w.kv_len_range
+        torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64)
+    count = int(round(w.k_outlier_frac * w.N))
+    rows = torch.empty((w.B, w.H, count), dtype=torch.int64)
+    for b in range(w.B):
+        for h in range(w.H):
+            rows[b, h] = torch.randperm(w.N, generator=g)[:count]
+    return rows
+
+
+def random_case(B: int, H: int, N: int, d: int, dtype: str, seed: int,
+                causal: bool = False, kv_len: Optional[list] = None,
+                backward: bool = False) -> Dict[str, Optional[torch.Tensor]]:
+    """Seeded inputs for an ad-hoc shape (tails, edge cases), same recipe."""
+    w = Workload(f"case_{B}x{H}x{N}x{d}_{dtype}", B, H, N, d, dtype,
+                 causal=causal, backward=backward)
+    out = make_inputs(w, seed)
+    if kv_len is not None:
+        out["kv_len"] = torch.tensor(kv_len, dtype=torch.int32)
+    return out

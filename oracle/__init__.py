@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check in
+``__graft_entry__.smoke`` and the CPU-baseline leg of ``bench.py`` may import
+this package. The library (``exact_io_aware_07_amd``) never imports it and
+shares no code with it; the two meet only at the seeded input generator.
+"""
+from .attention import attn_bwd64, attn_fwd64, attn_probs64, visible_mask  # noqa: F401
+from .brute import brute_head_forward, brute_head_grad_fd, brute_loss  # noqa: F401
+from .memory import score_matrix_bytes  # noqa: F401
