@@ -1,0 +1,154 @@
+"""ctypes binding of libfa.so: the same entry points as include/fa.h.
+
+Argument marshalling only: tensors are turned into device pointers and
+sizes, the stream into its HIP handle, and a non-OK status into an
+exception. Every step of the computation runs in the library's HIP kernels;
+there is no fallback of any kind, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from .build import LIB
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
+
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror")
+
+_DTYPE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+_lib: Optional[ctypes.CDLL] = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {fa_strerror(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is missing: build it with `python -m exact_io_aware_07_amd.build`")
+    L = ctypes.CDLL(LIB)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, i]
+    L.fa_fwd.restype = i
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp, i]
+    L.fa_bwd.restype = i
+    L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    L.fa_bwd_workspace_bytes.restype = sz
+    L.fa_strerror.argtypes = [i]
+    L.fa_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def fa_strerror(status: int) -> str:
+    return lib().fa_strerror(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensor(name: str, t: torch.Tensor, shape, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _kv(kv_len: Optional[torch.Tensor], B: int) -> Optional[int]:
+    if kv_len is None:
+        return None
+    _check_tensor("kv_len", kv_len, (B,), torch.int32)
+    return kv_len.data_ptr()
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+           scale: float, causal: bool = False, kv_len: Optional[torch.Tensor] = None,
+           stream=None) -> None:
+    """Enqueue the forward on ``stream`` (default: torch's current stream).
+
+    q, k, v: [B, H, N, d] device tensors of one dtype; o: [B, H, N, d] in that
+    dtype or fp32; lse: [B, H, N] fp32; kv_len: int32 [B] or None.
+    """
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("o", o, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                      int(bool(causal)), _kv(kv_len, B), _stream(stream, q.device),
+                      _DTYPE.get(q.dtype, -99), _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False,
+           kv_len: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> None:
+    """Enqueue the backward; writes dq, dk, dv ([B, H, N, d], input dtype).
+
+    ``workspace`` is a device tensor of at least fa_bwd_workspace_bytes()
+    bytes (allocated here when None).
+    """
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                      _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                      _kv(kv_len, B), _ptr(workspace), ws_bytes, _stream(stream, q.device),
+                      _DTYPE.get(q.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+
+
+# Convenience wrappers that allocate the outputs with torch (plumbing only).
+
+def attention_forward(q, k, v, causal: bool = False, kv_len=None, scale: Optional[float] = None,
+                      out_dtype: Optional[torch.dtype] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    B, H, N, d = q.shape
+    scale = d ** -0.5 if scale is None else scale
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal, kv_len, stream)
+    return o, lse
+
+
+def attention_backward(q, k, v, o, dout, lse, causal: bool = False, kv_len=None,
+                       scale: Optional[float] = None, stream=None):
+    d = q.shape[-1]
+    scale = d ** -0.5 if scale is None else scale
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len, None, stream)
+    return dq, dk, dv

@@ -1,0 +1,131 @@
+/*
+ * fa.h - exact IO-aware attention on one AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfa.so. Plain pointers and sizes only.
+ *
+ * The operation is exact scaled dot-product attention,
+ *     O = softmax(scale * Q K^T) V,
+ * computed tile by tile with the running row max / row sum rescaling of the
+ * online softmax, so the N x N score matrix is never written to device
+ * memory (marketmaker.cc article "Flash attention and the sequence-length
+ * question", sections "Flash 注意力算法" (the algorithm, tiling into row and
+ * column blocks) and "在线softmax递归" (online softmax recurrence); Ultralytics
+ * glossary page "Flash Attention", section "Come funziona Flash Attention").
+ * The forward keeps one number per query row for the backward, the natural
+ * log-sum-exp LSE; the backward recomputes the probability tiles from Q, K
+ * and LSE instead of storing them (marketmaker.cc article, section
+ * "向后传递：重新计算而不是存储" (backward: recompute instead of store)).
+ *
+ * Common conventions
+ *  - Tensors are dense, contiguous [B, H, N, d] with d innermost (the
+ *    (batch, heads, seq, head_dim) shape of the marketmaker.cc article,
+ *    section "集成是八行"). Every tensor pointer is a device pointer, 16-byte
+ *    aligned. The caller owns every buffer; the library allocates no device
+ *    memory and keeps no global mutable state, so calls are re-entrant.
+ *  - d must be 64 or 128. B, H, N >= 0; a call with B*H*N == 0 returns
+ *    FA_OK at once and does not inspect the pointers.
+ *  - scale must be finite and > 0 (usually 1/sqrt(d)).
+ *  - causal (0 or 1): key j is hidden from query i when j > i (top-left
+ *    aligned; queries and keys share the length N). Key blocks wholly in a
+ *    query block's future are skipped, never loaded (marketmaker.cc article,
+ *    section "因果掩盖是交易获得折扣的地方" (causal masking)).
+ *  - kv_len: NULL, or a device int32 array [B]; keys j >= kv_len[b] are
+ *    hidden from every query row of every head of batch b. Values are
+ *    clamped to [0, N]. Every query row is computed, padded ones included.
+ *  - A query row with no visible key gets O = 0 and LSE = -inf (no NaN).
+ *  - stream: a hipStream_t passed as void* (NULL = the null stream). Work is
+ *    enqueued asynchronously; FA_OK means "enqueued". A device fault shows
+ *    at the caller's next synchronisation.
+ *  - Argument validation happens on the host before any HIP call, so every
+ *    FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED / FA_ERR_WORKSPACE return has
+ *    launched nothing.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, scale, flag */
+  FA_ERR_UNSUPPORTED = -2, /* d not in {64,128}, or unsupported dtype pair */
+  FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required */
+  FA_ERR_HIP = -4          /* the kernel launch itself failed */
+} fa_status_t;
+
+/*
+ * Forward: O and LSE.
+ *   q, k, v  [B,H,N,d] in in_dtype (FA_BF16, FA_F16 or FA_F32).
+ *   o        [B,H,N,d] in o_dtype: in_dtype, or FA_F32 for bf16/fp16 inputs
+ *            (an fp32 copy of the same kernel's output, used to judge
+ *            accuracy apart from the output's own rounding).
+ *   lse      [B,H,N] fp32: LSE_i = log(sum_j exp(scale * q_i . k_j)) over
+ *            the visible keys j, natural log.
+ * bf16/fp16 inputs run QK^T and PV on MFMA with fp32 accumulation; the
+ * probabilities are rounded to the input type before PV. fp32 inputs are
+ * computed entirely in fp32.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           const int* kv_len, void* stream, int in_dtype, int o_dtype);
+
+/*
+ * Bytes of device workspace fa_bwd needs: one fp32 per query row
+ * (D_i = sum_c dO_ic * O_ic), i.e. B*H*N*4. Returns 0 for negative sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward: dQ, dK, dV of L = sum(dO * O) for the forward above.
+ *   q, k, v, o, dout  [B,H,N,d] in dtype; o is the forward's output.
+ *   lse               [B,H,N] fp32 from fa_fwd with the same arguments.
+ *   dq, dk, dv        [B,H,N,d] in dtype (written, not accumulated).
+ *   workspace         device buffer of at least fa_bwd_workspace_bytes(),
+ *                     16-byte aligned, owned by the caller; its contents on
+ *                     entry are ignored.
+ * Deterministic: the same inputs give bit-identical gradients.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal,
+           const int* kv_len, void* workspace, size_t workspace_bytes,
+           void* stream, int dtype);
+
+/*
+ * The backward as its three stages, for callers that want to time them or
+ * overlap the last two on separate streams. fa_bwd enqueues exactly
+ * fa_bwd_dsum, then fa_bwd_dkdv, then fa_bwd_dq on one stream. Arguments
+ * mean what they mean for fa_bwd; dsum is the fp32 [B,H,N] array
+ * D_i = sum_c dO_ic * O_ic (the workspace of fa_bwd), written by
+ * fa_bwd_dsum and read by the other two, which depend on nothing else that
+ * the other writes and may therefore run in either order or concurrently.
+ *   fa_bwd_dsum: reads o, dout; writes dsum (4-byte aligned).
+ *   fa_bwd_dkdv: reads q, k, v, dout, lse, dsum; writes dk, dv.
+ *   fa_bwd_dq:   reads q, k, v, dout, lse, dsum; writes dq.
+ * Errors as for fa_bwd (no FA_ERR_WORKSPACE: dsum is a plain argument).
+ */
+int fa_bwd_dsum(const void* o, const void* dout, float* dsum, int B, int H,
+                int N, int d, void* stream, int dtype);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                const float* lse, const float* dsum, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal,
+                const int* kv_len, void* stream, int dtype);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+              const float* lse, const float* dsum, void* dq, int B, int H,
+              int N, int d, float scale, int causal, const int* kv_len,
+              void* stream, int dtype);
+
+/* Static, human-readable text for a status code. Never NULL. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,118 @@
+"""Backward parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+The GPU backward consumes the GPU forward's own O (in the input dtype) and
+LSE; the oracle recomputes everything from the inputs in fp64. Each gradient
+is held to relative Frobenius error <= 2e-2 (bf16/fp16) or <= 1e-5 (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_07_amd import workloads as W
+from oracle import attn_bwd64, attn_bwd64_sampled
+from tests.helpers import F32_GRAD_REL_FRO, GRAD_REL_FRO, np64, rel_fro, run_bwd, run_fwd, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _grads(inp, scale, causal):
+    o, lse = run_fwd(inp, scale, causal)
+    return run_bwd(inp, o, lse, scale, causal)
+
+
+def _check_full(inp, scale, causal, tol, label, heads=None):
+    dq, dk, dv = _grads(inp, scale, causal)
+    ref = attn_bwd64(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, inp.get("kv_len"),
+                     heads=heads)
+    got = [np64(t) for t in (dq, dk, dv)]
+    if heads is not None:
+        got = [np.stack([g[b, h] for b, h in heads]) for g in got]
+    errs = {n: rel_fro(g, r) for n, g, r in zip(("dq", "dk", "dv"), got, ref)}
+    print(f"{label} rel-fro {errs}", flush=True)
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+    return got, ref
+
+
+SMALL = [(2, 2, n, d) for n in (1, 17, 129, 300) for d in (64, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_backward_small_shapes(shape, causal, dtype):
+    B, H, N, d = shape
+    say(f"bwd {shape} {dtype} causal={causal}")
+    inp = W.random_case(B, H, N, d, dtype, seed=3 * N + d, causal=causal, backward=True)
+    _check_full(inp, d ** -0.5, causal, GRAD_REL_FRO, str(shape))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_key_padding_masks_gradients(d, causal):
+    N = 300
+    kv = [0, 1, 150, 300]
+    say(f"bwd kv_len {kv} d={d} causal={causal}")
+    inp = W.random_case(4, 2, N, d, "bf16", seed=17, causal=causal, kv_len=kv, backward=True)
+    got, _ = _check_full(inp, d ** -0.5, causal, GRAD_REL_FRO, "kv")
+    dq, dk, dv = got
+    for b, L in enumerate(kv):
+        assert np.all(dk[b, :, L:] == 0.0) and np.all(dv[b, :, L:] == 0.0)
+    assert np.all(dq[0] == 0.0)  # no visible key anywhere in batch 0
+    assert all(np.isfinite(g).all() for g in got)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 64), (2, 1, 45, 64), (1, 2, 130, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_backward_fp32_path(shape, causal):
+    B, H, N, d = shape
+    say(f"bwd fp32 {shape} causal={causal}")
+    inp = W.random_case(B, H, N, d, "fp32", seed=N, causal=causal, backward=True)
+    _check_full(inp, d ** -0.5, causal, F32_GRAD_REL_FRO, f"fp32 {shape}")
+
+
+def test_config_gpt2_backward():
+    w = W.GPT2
+    say(w.name)
+    _check_full(W.make_inputs(w), w.scale, w.causal, GRAD_REL_FRO, w.name)
+
+
+def test_long_context_backward_two_heads():
+    w = W.LONG_BWD
+    say(w.name)
+    _check_full(W.make_inputs(w), w.scale, w.causal, GRAD_REL_FRO, w.name, heads=[(0, 0), (0, 31)])
+
+
+def test_trading_day_backward_sampled():
+    w = W.TRADE_BWD
+    say(w.name)
+    inp = W.make_inputs(w)
+    dq, dk, dv = (np64(t) for t in _grads(inp, w.scale, w.causal))
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 23399], rng.choice(w.N, 120, replace=False)]))
+    h = 5
+    rq, rk, rv = attn_bwd64_sampled(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.causal,
+                                    None, heads=[(0, h)], q_rows=rows, k_rows=rows)
+    errs = {"dq": rel_fro(dq[0, h, rows], rq[0]), "dk": rel_fro(dk[0, h, rows], rk[0]),
+            "dv": rel_fro(dv[0, h, rows], rv[0])}
+    print(f"{w.name} sampled rel-fro {errs}", flush=True)
+    for n, e in errs.items():
+        assert e <= GRAD_REL_FRO, (n, e)
+
+
+def test_backward_is_deterministic_and_satisfies_sum_rules():
+    w = W.GPT2.with_(B=2, N=700, causal=False)
+    say("bwd determinism")
+    inp = W.make_inputs(w)
+    a = _grads(inp, w.scale, False)
+    b = _grads(inp, w.scale, False)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    dk, dv = np64(a[1]), np64(a[2])
+    do = inp["do"].double().numpy()
+    # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, up to bf16 rounding of the
+    # per-key gradients
+    assert np.abs(dk.sum(axis=2)).max() <= 2e-2 * np.abs(dk).sum(axis=2).max()
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), rtol=0,
+                               atol=2e-2 * np.abs(dv).sum(axis=2).max())

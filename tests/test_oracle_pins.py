@@ -260,3 +260,30 @@ def test_score_matrix_bytes_match_printed_examples():
             assert got == c["printed_bytes"]
         else:
             assert abs(got / 1e9 - c["printed_gb_approx"]) <= c["rel_tol"] * c["printed_gb_approx"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_backward_matches_finite_differences_and_full(causal):
+    from oracle import attn_bwd64_sampled
+    # tiny: against central differences of the brute force directly
+    B, H, N, d = 1, 1, 6, 3
+    q, k, v, do = (_rand((B, H, N, d), 100 + s) for s in range(4))
+    kv = [5]
+    fq, fk, fv = brute_head_grad_fd(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.8, causal, kv[0])
+    sq, sk, sv = attn_bwd64_sampled(q, k, v, do, 0.8, causal, kv, heads=[(0, 0)],
+                                    q_rows=[0, 2, 5], k_rows=[1, 4, 5], row_chunk=2)
+    np.testing.assert_allclose(sq[0], np.array(fq)[[0, 2, 5]], rtol=0, atol=1e-8)
+    np.testing.assert_allclose(sk[0], np.array(fk)[[1, 4, 5]], rtol=0, atol=1e-8)
+    np.testing.assert_allclose(sv[0], np.array(fv)[[1, 4, 5]], rtol=0, atol=1e-8)
+    # larger: same numbers as the whole-matrix backward
+    B, H, N, d = 2, 2, 90, 8
+    q, k, v, do = (_rand((B, H, N, d), 110 + s) for s in range(4))
+    kv = [90, 40]
+    dq, dk, dv = attn_bwd64(q, k, v, do, 0.3, causal, kv)
+    rows, keys = [0, 7, 39, 40, 89], [0, 3, 39, 40, 88]
+    sq, sk, sv = attn_bwd64_sampled(q, k, v, do, 0.3, causal, kv, heads=[(1, 1), (0, 1)],
+                                    q_rows=rows, k_rows=keys, row_chunk=32)
+    for t, (b, h) in enumerate([(1, 1), (0, 1)]):
+        np.testing.assert_allclose(sq[t], dq[b, h, rows], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sk[t], dk[b, h, keys], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sv[t], dv[b, h, keys], rtol=0, atol=1e-12)
