@@ -34,7 +34,7 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["attn_fwd64", "attn_probs64", "attn_bwd64", "visible_mask"]
+__all__ = ["attn_fwd64", "attn_probs64", "attn_bwd64", "attn_bwd64_sampled", "visible_mask"]
 
 
 def _f64(x) -> np.ndarray:
@@ -160,4 +160,57 @@ def attn_bwd64(q, k, v, dout, scale: float, causal: bool = False, kv_len=None,
         dk[t] = scale * (ds.T @ q[b, h])
     if heads is None:
         return (dq.reshape(B, H, N, d), dk.reshape(B, H, N, d), dv.reshape(B, H, N, d))
+    return dq, dk, dv
+
+
+def attn_bwd64_sampled(q, k, v, dout, scale: float, causal: bool = False, kv_len=None,
+                       heads: Sequence[Tuple[int, int]] = ((0, 0),),
+                       q_rows: Sequence[int] = (), k_rows: Sequence[int] = (),
+                       row_chunk: int = 1024):
+    """The same gradients as ``attn_bwd64``, evaluated only for sampled query
+    rows (dQ) and sampled keys (dK, dV) of the listed heads, for sequences too
+    long for a full N x N fp64 matrix.
+
+    Per head: LSE_i and D_i = sum_j P_ij dP_ij come from whole rows of S (rows
+    are independent, so they are taken ``row_chunk`` at a time); then
+      dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j    for i in q_rows (whole rows)
+      dK_j = scale * sum_i P_ij (dP_ij - D_i) Q_i    for j in k_rows (whole columns)
+      dV_j = sum_i P_ij dO_i                         for j in k_rows
+    with P_ij = exp(S_ij - LSE_i) on visible entries and 0 elsewhere.
+    Returns (dQ [len(heads), R, d], dK [len(heads), C, d], dV [len(heads), C, d]).
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    lens = _kv_lens(kv_len, B, N)
+    qr = np.asarray(q_rows, dtype=np.int64)
+    kr = np.asarray(k_rows, dtype=np.int64)
+    pairs = list(heads)
+    dq = np.zeros((len(pairs), len(qr), d))
+    dk = np.zeros((len(pairs), len(kr), d))
+    dv = np.zeros((len(pairs), len(kr), d))
+    all_rows = np.arange(N)
+    for t, (b, h) in enumerate(pairs):
+        lim = int(lens[b])
+        lse = np.empty(N)
+        dsum = np.empty(N)
+        for c0 in range(0, N, row_chunk):
+            rr = all_rows[c0:c0 + row_chunk]
+            _, l_c, p_c = _rows_forward(q[b, h, rr], k[b, h], v[b, h], rr, scale, causal, lim)
+            dp_c = dout[b, h, rr] @ v[b, h].T
+            lse[rr] = l_c
+            dsum[rr] = (p_c * dp_c).sum(axis=1)
+        if len(qr):
+            _, _, p_r = _rows_forward(q[b, h, qr], k[b, h], v[b, h], qr, scale, causal, lim)
+            dp_r = dout[b, h, qr] @ v[b, h].T
+            dq[t] = scale * ((p_r * (dp_r - dsum[qr, None])) @ k[b, h])
+        if len(kr):
+            s_c = scale * (q[b, h] @ k[b, h, kr].T)                  # [N, C] columns of S
+            vis = visible_mask(all_rows, N, causal, lim)[:, kr]
+            has_key = np.isfinite(lse)
+            lse_safe = np.where(has_key, lse, 0.0)
+            p_c = np.where(vis & has_key[:, None], np.exp(s_c - lse_safe[:, None]), 0.0)
+            dp_c = dout[b, h] @ v[b, h, kr].T
+            ds_c = p_c * (dp_c - dsum[:, None])
+            dk[t] = scale * (ds_c.T @ q[b, h])
+            dv[t] = p_c.T @ dout[b, h]
     return dq, dk, dv
