@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Throughput of exact attention (forward + backward) on one MI355X.
+
+One step is the whole hot path on one batch of seeded synthetic input:
+fa_fwd, then the backward as the three launches fa_bwd enqueues
+(fa_bwd_dsum, fa_bwd_dkdv, fa_bwd_dq), all on one stream. The workload is the
+GPT-2-shaped forward+backward case: B=8, H=12, N=1024, d=64, bf16, causal,
+Q, K, V, dO ~ N(0, 1) from seed 0 (the only listed workload with a
+backward; the other shapes are parity-test cases and appear here only under
+"extra"). Inputs are resident in HBM before the timed region starts.
+
+Algorithmic work (what the method must do, not what the kernels happen to
+do): forward 4*B*H*N^2*d, backward 2.5x that (five N^2 d products: S
+recompute, dP, dV, dK, dQ), both halved for causal.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak on 1x MI355X"
+# MI355X dense peaks: bf16/fp16 MFMA 256 CU x 4096 FLOP/clk x 2.4 GHz, HBM3E 8 TB/s.
+PEAK_BF16_FLOPS = 256 * 4096 * 2.4e9
+PEAK_HBM_BYTES = 8.0e12
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+# roofline bound of each kernel of the step
+BOUND = {"fwd": "mfma", "dsum": "hbm", "dkdv": "mfma", "dq": "mfma"}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def fwd_flops(w) -> float:
+    return 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+
+
+def kernel_work(name: str, w) -> float:
+    """Algorithmic FLOPs (mfma kernels) or bytes (hbm kernels) per launch."""
+    half = 0.5 if w.causal else 1.0
+    pairs = w.B * w.H * w.N * w.N * half          # visible (query, key) pairs
+    if name == "fwd":
+        return 4.0 * w.d * pairs                   # S = QK^T and PV: 2d each
+    if name == "dkdv":
+        return 8.0 * w.d * pairs                   # S recompute, dP, dV, dK
+    if name == "dq":
+        return 2.0 * w.d * pairs                   # dQ (its S/dP recompute is overhead)
+    if name == "dsum":
+        return w.B * w.H * w.N * (2.0 * w.d * w.elem_bytes + 4.0)  # read O, dO; write D
+    raise KeyError(name)
+
+
+def traffic_for(name: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none for this kernel and workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)["kernels"][name]
+    except (OSError, KeyError, ValueError):
+        return None
+    from exact_io_aware_07_amd.profiling import source_sha
+    if rec.get("workload") != workload or rec.get("source_sha256") != source_sha(name):
+        return None
+    return rec.get("fetch_bytes_per_launch", 0) + rec.get("write_bytes_per_launch", 0)
+
+
+def run_gpu(args):
+    import torch
+    from exact_io_aware_07_amd import (fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dsum, fa_fwd, lib)
+    from exact_io_aware_07_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (no device visible)")
+    lib()  # fail loudly if libfa.so is missing
+    w = W.GPT2
+    inp = W.make_inputs(w, seed=0)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dsum = torch.empty_like(lse)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, stream)
+        if ev: ev[1].record(stream)
+        fa_bwd_dsum(o, do, dsum, stream)
+        if ev: ev[2].record(stream)
+        fa_bwd_dkdv(q, k, v, do, lse, dsum, dk, dv, w.scale, w.causal, None, stream)
+        if ev: ev[3].record(stream)
+        fa_bwd_dq(q, k, v, do, lse, dsum, dq, w.scale, w.causal, None, stream)
+        if ev: ev[4].record(stream)
+
+    log(f"[bench] warmup {args.warmup} steps of {w.name}")
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    names = ["fwd", "dsum", "dkdv", "dq"]
+    avg_ms = {n: statistics.fmean(ev[j].elapsed_time(ev[j + 1]) for ev in events)
+              for j, n in enumerate(names)}
+    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step; kernels (ms) {avg_ms}")
+
+    f_fwd = fwd_flops(w)
+    f_bwd = 2.5 * f_fwd
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    dom = max(names, key=lambda n: avg_ms[n])
+    bound = BOUND[dom]
+    work = kernel_work(dom, w)
+    achieved = work / (avg_ms[dom] * 1e-3)
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM_BYTES / 1e9,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_BYTES}
+    roof["kernel"] = dom
+    roof["traffic"] = traffic_for(dom, w.name)
+    kernels = {}
+    for n in names:
+        kw = kernel_work(n, w)
+        rate = kw / (avg_ms[n] * 1e-3)
+        if BOUND[n] == "mfma":
+            kernels[n] = {"avg_us": avg_ms[n] * 1e3, "tflops": rate / 1e12,
+                          "frac_bf16_peak": rate / PEAK_BF16_FLOPS}
+        else:
+            kernels[n] = {"avg_us": avg_ms[n] * 1e3, "gbps": rate / 1e9,
+                          "frac_hbm_peak": rate / PEAK_HBM_BYTES}
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "seed": 0,
+                   "flops_per_step": f_fwd + f_bwd,
+                   "flop_convention": "fwd 4BHN^2d, bwd 2.5x fwd, x0.5 causal"},
+        "pct_of_bf16_peak": 100.0 * value * 1e12 / PEAK_BF16_FLOPS,
+        "fwd_tflops": f_fwd / (avg_ms["fwd"] * 1e-3) / 1e12,
+        "bwd_tflops": f_bwd / ((avg_ms["dsum"] + avg_ms["dkdv"] + avg_ms["dq"]) * 1e-3) / 1e12,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_extra:
+        out["extra"] = extra_configs(torch, W)
+    return out
+
+
+def extra_configs(torch, W, iters: int = 10):
+    """Forward (and backward, at N >= 4096) TFLOP/s of the other workloads."""
+    from exact_io_aware_07_amd import attention_backward, attention_forward
+    res = {}
+    for w in (W.BERT, W.LONG, W.TRADE, W.LONG_BWD, W.TRADE_BWD):
+        inp = {n: (t.cuda() if t is not None else None) for n, t in W.make_inputs(w).items()}
+        fwd = lambda: attention_forward(inp["q"], inp["k"], inp["v"], w.causal, inp["kv_len"], w.scale)
+        o, lse = fwd()
+        if w.backward:
+            fn = lambda: attention_backward(inp["q"], inp["k"], inp["v"], o, inp["do"], lse,
+                                            w.causal, inp["kv_len"], w.scale)
+            flops = 2.5 * fwd_flops(w)
+        else:
+            fn = fwd
+            flops = fwd_flops(w)
+        for _ in range(2):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / iters
+        rate = flops / (ms * 1e-3)
+        entry = {"ms": ms, "tflops": rate / 1e12, "pct_of_bf16_peak": 100 * rate / PEAK_BF16_FLOPS}
+        if w.kv_len_range is not None:
+            eff = 4.0 * w.H * w.N * w.d * float(inp["kv_len"].sum().item())
+            entry["tflops_effective_kv_len"] = eff / (ms * 1e-3) / 1e12
+        res[w.name] = entry
+        log(f"[bench] extra {w.name}: {entry}")
+        del inp, o, lse
+    return res
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the same
+    workload: forward and backward of as many (b, h) heads as fit in about
+    ``target_s`` seconds, repeated (at least 3 times) while the total stays
+    near ``target_s``; the median pass is reported, in the GPU value's unit."""
+    import numpy as np  # noqa: F401
+    from exact_io_aware_07_amd import workloads as W
+    from oracle import attn_bwd64, attn_fwd64
+    w = W.GPT2
+    inp = W.make_inputs(w, seed=0)
+    q, k, v, do = (inp[n] for n in ("q", "k", "v", "do"))
+    heads_all = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(heads):
+        t = time.perf_counter()
+        attn_fwd64(q, k, v, w.scale, w.causal, heads=heads)
+        attn_bwd64(q, k, v, do, w.scale, w.causal, heads=heads)
+        return time.perf_counter() - t
+
+    t1 = run(heads_all[:1])
+    n = max(1, min(len(heads_all), int(target_s / max(t1, 1e-3))))
+    times = [run(heads_all[:n])]
+    while len(times) < 3 or sum(times) < target_s * 0.8:
+        times.append(run(heads_all[:n]))
+        if sum(times) > 2 * target_s:
+            break
+    elapsed = statistics.median(times)
+    flops = 3.5 * fwd_flops(w) * n / len(heads_all)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        threads = None
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s",
+            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"{w.name}: forward+backward of {n} of {len(heads_all)} heads "
+                      f"(fp64, materialised S), median of {len(times)} passes, {elapsed:.2f} s each",
+            "seconds": elapsed}
+
+
+def copy_calibration(nbytes: int) -> None:
+    """A plain device-to-device copy of ``nbytes`` (5 times), so that HBM
+    counters read under a profiler can be scaled to bytes: each copy kernel
+    reads and writes exactly ``nbytes``."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "copies": 5}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
+    ap.add_argument("--copy-calibration", type=int, metavar="BYTES", default=0,
+                    help="only run a plain copy of BYTES (for scaling HBM counters) and exit")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the per-head work is independent and would shard by (batch, head) with no "
+              "exchange, but only the single-GPU path exists", file=sys.stderr)
+        raise SystemExit(2)
+    out = run_gpu(args)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,8 @@ from .build import LIB
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_dsum", "fa_bwd_dkdv",
+           "fa_bwd_dq", "fa_strerror")
 
 _DTYPE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib: Optional[ctypes.CDLL] = None
@@ -45,6 +46,12 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = i
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     L.fa_bwd_workspace_bytes.restype = sz
+    L.fa_bwd_dsum.argtypes = [vp, vp, vp, i, i, i, i, vp, i]
+    L.fa_bwd_dsum.restype = i
+    L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
+    L.fa_bwd_dkdv.restype = i
+    L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
+    L.fa_bwd_dq.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -131,6 +138,50 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False
                       _DTYPE.get(q.dtype, -99))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_dsum(o, dout, dsum, stream=None) -> None:
+    """Stage 1 of the backward: dsum[b, h, i] = sum_c dout * o (fp32 [B, H, N])."""
+    B, H, N, d = o.shape
+    _check_tensor("o", o, o.shape)
+    _check_tensor("dout", dout, o.shape, o.dtype)
+    _check_tensor("dsum", dsum, (B, H, N), torch.float32)
+    st = lib().fa_bwd_dsum(_ptr(o), _ptr(dout), _ptr(dsum), B, H, N, d, _stream(stream, o.device),
+                           _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dsum")
+
+
+def fa_bwd_dkdv(q, k, v, dout, lse, dsum, dk, dv, scale: float, causal: bool = False,
+                kv_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Stage 2 of the backward: writes dk, dv."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    _check_tensor("dsum", dsum, (B, H, N), torch.float32)
+    st = lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dsum), _ptr(dk),
+                           _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _kv(kv_len, B),
+                           _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dkdv")
+
+
+def fa_bwd_dq(q, k, v, dout, lse, dsum, dq, scale: float, causal: bool = False,
+              kv_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Stage 3 of the backward: writes dq."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    _check_tensor("dsum", dsum, (B, H, N), torch.float32)
+    st = lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dsum), _ptr(dq),
+                         B, H, N, d, float(scale), int(bool(causal)), _kv(kv_len, B),
+                         _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dq")
 
 
 # Convenience wrappers that allocate the outputs with torch (plumbing only).

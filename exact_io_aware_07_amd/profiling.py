@@ -1,0 +1,131 @@
+"""Summaries of rocprofv3 output for the library's kernels.
+
+    python -m exact_io_aware_07_amd.profiling stats CSV --cmd "..." --out FILE.md
+    python -m exact_io_aware_07_amd.profiling traffic --fetch CSV --write CSV \
+        --copy-fetch CSV --copy-write CSV --copy-bytes N --workload NAME \
+        --cmd "..." --out-md FILE.md --out-json profiles/traffic.json
+
+``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a short
+markdown table. ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
+WRITE_SIZE, KiB per dispatch) into HBM bytes per launch, each counter scaled
+by what it reads for a plain device copy of known size, and records the hash
+of the kernel sources the counters were taken on, so a stale figure is
+never reported for a changed kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+from typing import Dict, List
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+# short name -> (substring of the demangled kernel name, defining source)
+KERNELS = {
+    "fwd": ("fwd_mfma_kernel", "fa_fwd_mfma.hip"),
+    "dsum": ("dsum_kernel", "fa_bwd_mfma.hip"),
+    "dkdv": ("dkdv_kernel", "fa_bwd_mfma.hip"),
+    "dq": ("dq_kernel", "fa_bwd_mfma.hip"),
+}
+
+
+def source_sha(short: str) -> str:
+    """sha256 of the source that defines kernel ``short`` plus the shared header."""
+    h = hashlib.sha256()
+    for f in (KERNELS[short][1], "fa_internal.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def short_name(kernel_name: str) -> str:
+    for short, (sub, _) in KERNELS.items():
+        if f"::{sub}<" in kernel_name or kernel_name.startswith(sub):
+            return short
+    return kernel_name
+
+
+def _counter_means(path: str, counter: str) -> Dict[str, float]:
+    vals: Dict[str, List[float]] = collections.defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def _copy_factor(path: str, counter: str, nbytes: int) -> float:
+    means = _counter_means(path, counter)
+    copies = [v for k, v in means.items() if "copy" in k.lower()]
+    if not copies:
+        raise SystemExit(f"no copy kernel found in {path}")
+    return nbytes / (max(copies) * 1024.0)
+
+
+def stats_md(csv_path: str, cmd: str) -> str:
+    lines = ["# Kernel time (rocprofv3 --kernel-trace --stats)", "", "Command:", "", "```",
+             cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+    return "\n".join(lines) + "\n"
+
+
+def traffic(args) -> None:
+    ff = _copy_factor(args.copy_fetch, "FETCH_SIZE", args.copy_bytes)
+    fw = _copy_factor(args.copy_write, "WRITE_SIZE", args.copy_bytes)
+    fetch = _counter_means(args.fetch, "FETCH_SIZE")
+    write = _counter_means(args.write, "WRITE_SIZE")
+    out = {"workload": args.workload, "copy_bytes": args.copy_bytes,
+           "fetch_scale": ff, "write_scale": fw, "kernels": {}}
+    md = ["# HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",
+          f"Workload: `{args.workload}`.", "", "Commands:", "", "```", args.cmd, "```", "",
+          f"Scale factors from a plain {args.copy_bytes} B device copy (the copy reads and "
+          f"writes exactly that many bytes): FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f}.", "",
+          "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |",
+          "|---|---|---|---|---|"]
+    for name in sorted(set(fetch) | set(write)):
+        short = short_name(name)
+        fb = fetch.get(name, 0.0) * 1024.0 * ff
+        wb = write.get(name, 0.0) * 1024.0 * fw
+        md.append(f"| `{short}` | {fetch.get(name, 0.0):.1f} | {write.get(name, 0.0):.1f} | "
+                  f"{fb / 1e6:.2f} | {wb / 1e6:.2f} |")
+        if short in KERNELS:
+            out["kernels"][short] = {"workload": args.workload, "kernel_name": name,
+                                     "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                                     "source_sha256": source_sha(short)}
+    with open(args.out_md, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    with open(args.out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for name in ("fetch", "write", "copy_fetch", "copy_write", "workload", "cmd", "out_md", "out_json"):
+        t.add_argument("--" + name.replace("_", "-"), dest=name, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    a = ap.parse_args()
+    if a.what == "stats":
+        with open(a.out, "w") as fh:
+            fh.write(stats_md(a.csv, a.cmd))
+    else:
+        traffic(a)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,7 @@ def _declared():
     return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_exported_entry_points():
     assert _declared() == sorted(fa.EXPORTS)
 
 
@@ -124,3 +124,18 @@ def test_package_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
                 assert "attn_fwd64" not in text and "attn_bwd64" not in text, f
+
+
+def test_stage_entry_points_validate_before_launch():
+    L = fa.lib()
+    assert L.fa_bwd_dsum(None, A, A, 1, 1, 16, 64, None, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dsum(A, A, A + 2, 1, 1, 16, 64, None, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dsum(A, A, A, 1, 1, 16, 80, None, fa.FA_BF16) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_bwd_dsum(None, None, None, 0, 1, 16, 64, None, fa.FA_BF16) == fa.FA_OK
+    assert L.fa_bwd_dkdv(A, A, A, A, A, None, A, A, 1, 1, 16, 64, 0.125, 0, None, None,
+                         fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dkdv(A, A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 3, None, None,
+                         fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dq(A, A, A, A, A, A, None, 1, 1, 16, 64, 0.125, 0, None, None,
+                       fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dq(A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None, 9) == fa.FA_ERR_UNSUPPORTED
