@@ -261,6 +261,32 @@ def copy_calibration(nbytes: int) -> None:
     print(json.dumps({"copy_bytes": nbytes, "copies": 5}), flush=True)
 
 
+def profile_workload(name: str, iters: int) -> None:
+    """Run one workload's forward (and backward, if it has one) ``iters`` times,
+    for use under a profiler; prints one JSON line with the mean times."""
+    import torch
+    from exact_io_aware_07_amd import attention_backward, attention_forward, lib
+    from exact_io_aware_07_amd import workloads as W
+    lib()
+    w = W.ALL[name]
+    inp = {n: (t.cuda() if t is not None else None) for n, t in W.make_inputs(w).items()}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd_ms, bwd_ms = [], []
+    for _ in range(iters):
+        ev[0].record()
+        o, lse = attention_forward(inp["q"], inp["k"], inp["v"], w.causal, inp["kv_len"], w.scale)
+        ev[1].record()
+        if w.backward:
+            attention_backward(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, w.causal,
+                               inp["kv_len"], w.scale)
+        ev[2].record()
+        torch.cuda.synchronize()
+        fwd_ms.append(ev[0].elapsed_time(ev[1]))
+        bwd_ms.append(ev[1].elapsed_time(ev[2]))
+    print(json.dumps({"workload": name, "iters": iters, "fwd_ms": statistics.fmean(fwd_ms),
+                      "bwd_ms": statistics.fmean(bwd_ms) if w.backward else None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,7 +296,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES", default=0,
                     help="only run a plain copy of BYTES (for scaling HBM counters) and exit")
+    ap.add_argument("--profile-workload", metavar="NAME", default="",
+                    help="only run NAME's forward (+backward) --iters times and exit")
+    ap.add_argument("--iters", type=int, default=10)
     args = ap.parse_args()
+    if args.profile_workload:
+        profile_workload(args.profile_workload, args.iters)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return

@@ -25,6 +25,9 @@ int check_scalars(int B, int H, int N, int d, float scale, int causal) {
   // so it has the largest grid of any launch.
   const long long rows = (long long)B * H * N;
   if (rows / 8 + 1 > kMaxBlocks) return FA_ERR_INVALID_ARG;
+  // One head's [N, d] slab is addressed with 32-bit byte offsets (buffer
+  // resources); fp32 tensors need N * d * 4 bytes.
+  if ((long long)N * d * 4 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

@@ -3,7 +3,7 @@
 // The method: split Q into row blocks and K, V into column blocks; for each
 // query block stream every key/value block through on-chip memory, keep a
 // running row max m and row sum l, rescale the partial output by
-// exp(m_old - m_new) whenever the max grows, and divide by l once at the end
+// exp(m_old - m_new) when the max grows, and divide by l once at the end
 // (marketmaker.cc article "Flash attention and the sequence-length
 // question", sections "Flash 注意力算法" and "在线softmax递归"; the division
 // deferred to the end of the loop is the first FA2 change listed in its
@@ -15,18 +15,31 @@
 //
 // gfx950 mapping
 //  * workgroup = 4 waves = 128 query rows; wave w owns rows [32w, 32w+32).
-//  * S^T = K Q^T on v_mfma_f32_32x32x16 (A = K tile from LDS, B = the wave's
-//    Q rows held in VGPRs for the whole kernel). In the 32x32 accumulator
-//    layout lane l holds query column l % 32 and 16 keys, so a query's row
-//    max and row sum are in-lane plus one exchange with lane l ^ 32.
-//  * O^T += V^T P^T on the same MFMA. The probabilities leave the S
-//    accumulator already in B-operand order (lane l % 32 = query, keys in
-//    runs of 4), so P never goes through LDS. V is written to LDS transposed,
-//    in runs of 4 keys per d, so each A fragment is two 8-byte LDS reads.
-//  * K/V tiles are double-buffered in LDS with one barrier per tile; the next
-//    tile's global loads are in flight while the current tile is computed.
-//  * Scores stay in raw units; exp2 of (s * scale * log2 e - m * scale *
-//    log2 e) is one FMA and one v_exp_f32 per score.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16 (A = 32 keys of the K tile in LDS,
+//    B = the wave's Q rows, resident in VGPRs). In the 32x32 accumulator
+//    lane l holds query l % 32 and 16 keys, so a row's max and sum are
+//    in-lane plus one exchange with lane l ^ 32.
+//  * O^T += V^T P^T on the same MFMA. P leaves the S accumulator already in
+//    B-operand order (lane = query, keys in runs of 4). V stays row-major in
+//    LDS; ds_read_b64_tr_b16 hands each lane 4 consecutive keys of one d
+//    column, which is exactly the A-operand order that matches P.
+//  * Software pipeline: while tile j's softmax and P V run, S for tile j+1 is
+//    already being computed from the next K tile, so the MFMA unit has
+//    independent work during the exponentials. K tiles run one tile ahead of
+//    V tiles through two LDS buffers each; one barrier per tile.
+//  * Global loads are buffer loads against a per-head resource whose size
+//    ends at the last visible key, so rows past the end read as zero with no
+//    branch.
+//  * Scores stay in raw units; exp2(s * scale * log2 e - m * scale * log2 e)
+//    is one FMA and one v_exp_f32 per score.
+//  * The running max is exact, so the largest probability of a row is
+//    exactly 1 and is not rounded when P is cast for the P V product (a
+//    stale reference would put the dominant key's probability at an
+//    arbitrary value and round it, which matters when one key dominates a
+//    row). The rescale of O is skipped, wave-uniformly, when no row max of
+//    the wave moved.
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -37,31 +50,40 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;  // query rows per workgroup
 
 template <int D>
-struct FwdTile;
-template <>
-struct FwdTile<128> {
-  static constexpr int BC = 64;  // keys per tile: K and V tiles are 16 KiB each
+struct FwdTile {
+  static constexpr int BC = 64;  // keys per tile
 };
-template <>
-struct FwdTile<64> {
-  static constexpr int BC = 128;
-};
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// 4 x 16-bit from LDS, transposed across each group of 16 lanes.
+__device__ inline u32x2 lds_read_tr(const uint16_t* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) void*)p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <typename T, int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int BC = FwdTile<D>::BC;
-  constexpr int KT = BC / 32;                        // 32-key sub-tiles
-  constexpr int DC = D / 16;                         // 16-wide d chunks (S reduction)
-  constexpr int DT = D / 32;                         // 32-wide d tiles of O^T
-  constexpr int K_LD = D + 8;                        // u16 per K row in LDS (16 B pad)
-  constexpr int VT_LD = BC + 4;                      // u16 per V^T row in LDS (8 B pad)
-  constexpr int KCH = BC * D / 8 / kThreads;         // 16-byte K chunks per thread
-  constexpr int VU = (BC / 4) * (D / 8) / kThreads;  // 4-row x 8-col V units per thread
-  static_assert(KCH >= 1 && VU >= 1, "tile too small for the workgroup");
-  static_assert(BC * D / 8 % kThreads == 0 && (BC / 4) * (D / 8) % kThreads == 0, "");
+  constexpr int KT = BC / 32;                   // 32-key sub-tiles
+  constexpr int DC = D / 16;                    // 16-wide d chunks (S reduction)
+  constexpr int DT = D / 32;                    // 32-wide d tiles of O^T
+  constexpr int K_LD = D + 8;                   // u16 per K row in LDS (16 B pad)
+  constexpr int V_LD = D + 32;                  // u16 per V row in LDS (64 B pad)
+  constexpr int CH = BC * D / 8 / kThreads;     // 16-byte chunks per thread per tile
+  static_assert(CH >= 1 && BC * D / 8 % kThreads == 0, "tile too small for the workgroup");
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * K_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VT_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * V_LD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -78,12 +100,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int b = bh / a.H;
 
   const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + head_off;
-  const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + head_off;
-  const uint16_t* __restrict__ Vg = (const uint16_t*)a.v + head_off;
-
   int kv_end = N;
   if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + head_off, (uint32_t)kv_end * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + head_off, (uint32_t)kv_end * D * 2);
+
   const int q_blk0 = qb * kBR;
   const int q_blk_last = min(q_blk0 + kBR, N) - 1;
   int kv_lim = kv_end;  // keys the workgroup needs (exclusive)
@@ -94,92 +116,96 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int my_q = wq0 + ql;
   int w_lim = kv_end;  // keys this wave needs (exclusive)
   if (a.causal) w_lim = min(w_lim, min(wq0 + 31, N - 1) + 1);
+  const int w_tiles = (w_lim + BC - 1) / BC;  // tiles this wave computes
 
   u32x4 qf[DC];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    qf[dc] = (my_q < N) ? *(const u32x4*)(Qg + (size_t)my_q * D + dc * 16 + hh * 8)
-                        : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int dc = 0; dc < DC; ++dc) qf[dc] = buf_load16(rq, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY;  // running max of raw scores (both halves agree)
-  float l_run = 0.f;        // running sum over this half's keys
+  float m_ref = -INFINITY;  // running max of raw scores (both halves agree)
+  float l_run = 0.f;        // running sum over this half's keys, against m_ref
   const float sl2 = a.scale * kLog2e;
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[VU][4];
-
-  auto load_tile = [&](int j) {
-    const int t0 = j * BC;
-    const int rows = kv_end - t0;  // rows at or past kv_end load as zeros
+  // Staging registers: K(j+1) and V(j) at the top of iteration j.
+  u32x4 kreg[CH], vreg[CH];
+  auto chunk_off = [&](int i) {  // element offset of this thread's chunk i in a tile
+    const int c = tid + kThreads * i;
+    return (c / (D / 8)) * D + (c % (D / 8)) * 8;
+  };
+  auto load_k = [&](int j) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < CH; ++i) kreg[i] = buf_load16(rk, (uint32_t)(j * BC * D + chunk_off(i)) * 2);
+  };
+  auto load_v = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) vreg[i] = buf_load16(rv, (uint32_t)(j * BC * D + chunk_off(i)) * 2);
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
       const int c = tid + kThreads * i;
-      const int r = c / (D / 8), c8 = c % (D / 8);
-      kreg[i] = (r < rows) ? *(const u32x4*)(Kg + (size_t)(t0 + r) * D + c8 * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)&Ks[buf][(c / (D / 8)) * K_LD + (c % (D / 8)) * 8] = kreg[i];
     }
+  };
+  auto store_v = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + kThreads * i;
-      const int g = u % (BC / 4), c8 = u / (BC / 4);
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + kThreads * i;
+      *(u32x4*)&Vs[buf][(c / (D / 8)) * V_LD + (c % (D / 8)) * 8] = vreg[i];
+    }
+  };
+  auto compute_s = [&](int buf, f32x16 (&s)[KT]) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * g + r;
-        vreg[i][r] = (row < rows) ? *(const u32x4*)(Vg + (size_t)(t0 + row) * D + c8 * 8)
-                                  : u32x4{0u, 0u, 0u, 0u};
+    for (int kt = 0; kt < KT; ++kt) {
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const u32x4 kf = *(const u32x4*)&Ks[buf][(kt * 32 + ql) * K_LD + dc * 16 + hh * 8];
+        s[kt] = Mfma<T>::mma32(kf, qf[dc], s[kt]);
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / (D / 8), c8 = c % (D / 8);
-      *(u32x4*)&Ks[buf][r * K_LD + c8 * 8] = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + kThreads * i;
-      const int g = u % (BC / 4), c8 = u / (BC / 4);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {  // dword p holds columns 2p (low half) and 2p+1
-        const uint32_t w0 = vreg[i][0][p], w1 = vreg[i][1][p];
-        const uint32_t w2 = vreg[i][2][p], w3 = vreg[i][3][p];
-        const u32x2 lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-        const u32x2 hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-        *(u32x2*)&Vt[buf][(c8 * 8 + 2 * p) * VT_LD + 4 * g] = lo;
-        *(u32x2*)&Vt[buf][(c8 * 8 + 2 * p + 1) * VT_LD + 4 * g] = hi;
-      }
-    }
-  };
-
-  if (ntiles > 0) load_tile(0);
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    store_tile(buf);
+  f32x16 s_a[KT], s_b[KT];
+  if (ntiles > 0) {
+    load_k(0);
+    store_k(0);
+    if (ntiles > 1) load_k(1);
+    load_v(0);
     __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1);
+    if (w_tiles > 0) compute_s(0, s_a);
+  }
 
-    const int t0 = j * BC;
-    if (t0 < w_lim) {
-      // S^T tile: 32 keys x 32 queries per sub-tile, raw dot products.
-      f32x16 s[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        s[kt] = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const u32x4 kf = *(const u32x4*)&Ks[buf][(kt * 32 + ql) * K_LD + dc * 16 + hh * 8];
-          s[kt] = Mfma<T>::mma32(kf, qf[dc], s[kt]);
-        }
-      }
+  // V fragment addressing for ds_read_b64_tr_b16: in each 16-lane group,
+  // lane i reads key row (4*half + i/4) and d columns [16*dh + 4*(i%4), +4).
+  const int g16 = lane & 15;
+  const int v_row = 4 * hh + (g16 >> 2);
+  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
 
+  // One tile of the pipeline: S of tile j+1 into s_nxt, softmax and P V of
+  // tile j from s_cur. FULL tiles (every row of every wave sees every key of
+  // tiles j and j+1) run branch-free apart from the uniform rescale test, so
+  // the S(j+1) products, the exponentials of tile j and its P V products sit
+  // in one basic block and the scheduler can interleave MFMA and VALU work.
+  // Other tiles (the causal diagonal, the padded or ragged end) take the
+  // general path with per-wave liveness and masking.
+  auto tile = [&](int j, f32x16 (&s_cur)[KT], f32x16 (&s_nxt)[KT], auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    if (FULL || j + 1 < ntiles) store_k((j + 1) & 1);
+    store_v(j & 1);
+    __syncthreads();
+    // Loads past the last tile read inside the head (or as zeros past the
+    // resource end) and are never used.
+    if (FULL || j + 2 < ntiles) load_k(j + 2);
+    if (FULL || j + 1 < ntiles) load_v(j + 1);
+    const bool live = FULL || j < w_tiles;
+    if (!live) return;
+
+    if constexpr (!FULL) {
+      const int t0 = j * BC;
       const bool need_mask = (t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0);
       if (need_mask) {
 #pragma unroll
@@ -188,58 +214,81 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
           for (int r = 0; r < 16; ++r) {
             const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
             const bool vis = key < kv_end && (!a.causal || key <= my_q);
-            if (!vis) s[kt][r] = -INFINITY;
-          }
-        }
-      }
-
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      }
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == m_run) ? 1.f : fast_exp2((m_run - m_new) * sl2);
-      const float mref = (m_new == -INFINITY) ? 0.f : m_new * sl2;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kt][r], sl2, -mref));
-          s[kt][r] = p;
-          lsum += p;
-        }
-      }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      }
-
-      // O^T += V^T P^T, 16 keys per MFMA.
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const u32x4 pf = {Mfma<T>::pack(s[kt][8 * c2 + 0], s[kt][8 * c2 + 1]),
-                            Mfma<T>::pack(s[kt][8 * c2 + 2], s[kt][8 * c2 + 3]),
-                            Mfma<T>::pack(s[kt][8 * c2 + 4], s[kt][8 * c2 + 5]),
-                            Mfma<T>::pack(s[kt][8 * c2 + 6], s[kt][8 * c2 + 7])};
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* vp = &Vt[buf][(dt * 32 + ql) * VT_LD + kt * 32 + c2 * 16 + 4 * hh];
-            const u32x2 v0 = *(const u32x2*)vp;
-            const u32x2 v1 = *(const u32x2*)(vp + 8);
-            const u32x4 vf = {v0.x, v0.y, v1.x, v1.y};
-            oacc[dt] = Mfma<T>::mma32(vf, pf, oacc[dt]);
+            if (!vis) s_cur[kt][r] = -INFINITY;
           }
         }
       }
     }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
+    }
+    mx = fmaxf(mx, swap_halves(mx));
+    if (__any(mx > m_ref)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_new == m_ref) ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m_ref = m_new;
+    }
+
+    if (FULL || j + 1 < w_tiles) compute_s((j + 1) & 1, s_nxt);
+
+    const float mref2 = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s_cur[kt][r], sl2, -mref2));
+        s_cur[kt][r] = p;
+        lsum += p;
+      }
+    }
+    l_run += lsum;
+
+    // O^T += V^T P^T, 16 keys per MFMA.
+    const uint16_t* vb = &Vs[j & 1][v_row * V_LD + v_col];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const u32x4 pf = {Mfma<T>::pack(s_cur[kt][8 * c2 + 0], s_cur[kt][8 * c2 + 1]),
+                          Mfma<T>::pack(s_cur[kt][8 * c2 + 2], s_cur[kt][8 * c2 + 3]),
+                          Mfma<T>::pack(s_cur[kt][8 * c2 + 4], s_cur[kt][8 * c2 + 5]),
+                          Mfma<T>::pack(s_cur[kt][8 * c2 + 6], s_cur[kt][8 * c2 + 7])};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* vp = vb + (kt * 32 + c2 * 16) * V_LD + dt * 32;
+          const u32x2 v0 = lds_read_tr(vp);
+          const u32x2 v1 = lds_read_tr(vp + 8 * V_LD);
+          const u32x4 vf = {v0.x, v0.y, v1.x, v1.y};
+          oacc[dt] = Mfma<T>::mma32(vf, pf, oacc[dt]);
+        }
+      }
+    }
+  };
+
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
+  // Tiles fully visible to every row of the workgroup, and followed by a
+  // further tile, form the branch-free main loop (an even count, so the two
+  // S arrays swap roles without copies).
+  int n_full = (a.causal ? min(kv_end, q_blk0 + 1) : kv_end) / BC;
+  n_full = min(n_full, ntiles - 1) & ~1;
+  int j = 0;
+  for (; j < n_full; j += 2) {
+    tile(j, s_a, s_b, Full{});
+    tile(j + 1, s_b, s_a, Full{});
+  }
+  for (; j < ntiles; ++j) {
+    tile(j, s_a, s_b, Part{});
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) s_a[kt] = s_b[kt];
   }
 
   const float l_tot = l_run + swap_halves(l_run);
@@ -263,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
     }
     if (hh == 0) {
       a.lse[(size_t)bh * N + my_q] =
-          (l_tot > 0.f) ? m_run * a.scale + fast_log2(l_tot) * kLn2 : -INFINITY;
+          (l_tot > 0.f) ? m_ref * a.scale + fast_log2(l_tot) * kLn2 : -INFINITY;
     }
   }
 }

@@ -23,7 +23,9 @@
  *    aligned. The caller owns every buffer; the library allocates no device
  *    memory and keeps no global mutable state, so calls are re-entrant.
  *  - d must be 64 or 128. B, H, N >= 0; a call with B*H*N == 0 returns
- *    FA_OK at once and does not inspect the pointers.
+ *    FA_OK at once and does not inspect the pointers. One head's slab must
+ *    be under 2 GiB at 4 bytes per element (N * d * 4 < 2^31, so
+ *    N <= 4,194,303 at d = 128); larger N returns FA_ERR_UNSUPPORTED.
  *  - scale must be finite and > 0 (usually 1/sqrt(d)).
  *  - causal (0 or 1): key j is hidden from query i when j > i (top-left
  *    aligned; queries and keys share the length N). Key blocks wholly in a

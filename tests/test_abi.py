@@ -139,3 +139,8 @@ def test_stage_entry_points_validate_before_launch():
     assert L.fa_bwd_dq(A, A, A, A, A, A, None, 1, 1, 16, 64, 0.125, 0, None, None,
                        fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
     assert L.fa_bwd_dq(A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None, 9) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_sequence_longer_than_a_32_bit_head_is_unsupported():
+    assert _fwd(N=4194304, d=128) == fa.FA_ERR_UNSUPPORTED
+    assert _fwd(N=8388608, d=64) == fa.FA_ERR_UNSUPPORTED
