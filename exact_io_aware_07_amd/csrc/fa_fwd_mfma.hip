@@ -27,9 +27,14 @@
 //    already being computed from the next K tile, so the MFMA unit has
 //    independent work during the exponentials. K tiles run one tile ahead of
 //    V tiles through two LDS buffers each; one barrier per tile.
-//  * Global loads are buffer loads against a per-head resource whose size
-//    ends at the last visible key, so rows past the end read as zero with no
-//    branch.
+//  * K and V tiles go from HBM straight into LDS (buffer_load ... lds), no
+//    VGPR staging: each load instruction fills 1 KiB of LDS (4 rows at
+//    d = 128, 8 at d = 64); those 1 KiB groups are padded by 16 bytes and the
+//    16-byte chunks of a row are XOR-swizzled by the row's place in its group,
+//    so the K fragment reads (32 rows, one chunk) and the transposed V reads
+//    (4 rows, two chunks per 16 lanes) hit distinct LDS banks.
+//  * Global loads use buffer resources whose size ends at the last visible
+//    key, so rows past the end read as zero with no branch.
 //  * Scores stay in raw units; exp2(s * scale * log2 e - m * scale * log2 e)
 //    is one FMA and one v_exp_f32 per score.
 //  * The running max is exact, so the largest probability of a row is
@@ -71,19 +76,36 @@ __device__ inline u32x2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// LDS tile layout for direct loads: [rows][D] bf16/fp16, in groups of RPI
+// rows (1 KiB, one load instruction), each group padded by 16 bytes; within
+// a group, logical 16-byte chunk c of row r' sits at position c ^ sw(r').
+template <int D>
+struct TileLayout {
+  static constexpr int RB = D * 2;            // bytes per row
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;       // rows per 1 KiB group
+  static constexpr int GB = 1024 + 16;        // bytes per group incl. pad
+  __device__ static constexpr int sw(int r) { return D == 128 ? 4 * r : 2 * (r >> 1); }
+  // byte offset of logical (row, chunk) inside a tile
+  __device__ static constexpr int off(int row, int chunk) {
+    return (row / RPI) * GB + (row % RPI) * RB + ((chunk ^ sw(row % RPI)) << 4);
+  }
+  static constexpr int bytes(int rows) { return rows / RPI * GB; }
+};
+
 template <typename T, int D, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(FwdArgs a) {
+  using L = TileLayout<D>;
   constexpr int BC = FwdTile<D>::BC;
   constexpr int KT = BC / 32;                   // 32-key sub-tiles
   constexpr int DC = D / 16;                    // 16-wide d chunks (S reduction)
   constexpr int DT = D / 32;                    // 32-wide d tiles of O^T
-  constexpr int K_LD = D + 8;                   // u16 per K row in LDS (16 B pad)
-  constexpr int V_LD = D + 32;                  // u16 per V row in LDS (64 B pad)
-  constexpr int CH = BC * D / 8 / kThreads;     // 16-byte chunks per thread per tile
-  static_assert(CH >= 1 && BC * D / 8 % kThreads == 0, "tile too small for the workgroup");
+  constexpr int TB = L::bytes(BC);              // bytes per K or V tile
+  constexpr int GPW = BC / L::RPI / kWaves;     // load instructions per wave per tile
+  static_assert(GPW >= 1 && BC % (L::RPI * kWaves) == 0, "tile too small for the workgroup");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * K_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * V_LD];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -129,61 +151,62 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
   float l_run = 0.f;        // running sum over this half's keys, against m_ref
   const float sl2 = a.scale * kLog2e;
 
-  // Staging registers: K(j+1) and V(j) at the top of iteration j.
-  u32x4 kreg[CH], vreg[CH];
-  auto chunk_off = [&](int i) {  // element offset of this thread's chunk i in a tile
-    const int c = tid + kThreads * i;
-    return (c / (D / 8)) * D + (c % (D / 8)) * 8;
-  };
-  auto load_k = [&](int j) {
+  // Direct loads: lane l of a wave's instruction for group G fills position
+  // l of the group (row l / CPR, position l % CPR) with the logical chunk
+  // (l % CPR) ^ sw(row) of that row.
+  const int ld_row = lane / L::CPR;
+  const int ld_chunk = (lane % L::CPR) ^ L::sw(ld_row);
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int j) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) kreg[i] = buf_load16(rk, (uint32_t)(j * BC * D + chunk_off(i)) * 2);
-  };
-  auto load_v = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) vreg[i] = buf_load16(rv, (uint32_t)(j * BC * D + chunk_off(i)) * 2);
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + kThreads * i;
-      *(u32x4*)&Ks[buf][(c / (D / 8)) * K_LD + (c % (D / 8)) * 8] = kreg[i];
+    for (int g = 0; g < GPW; ++g) {
+      const int G = wave * GPW + g;
+      const int row = j * BC + G * L::RPI + ld_row;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(dst + G * L::GB), 16,
+          (row * D + ld_chunk * 8) * 2, 0, 0, 0);
     }
   };
-  auto store_v = [&](int buf) {
+
+  // K fragment (A of S^T): row kt*32 + ql, chunk 2*dc + hh. The row's place
+  // in its group is fixed per lane, so the swizzle folds into a per-lane
+  // offset per chunk.
+  int k_off[DC];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + kThreads * i;
-      *(u32x4*)&Vs[buf][(c / (D / 8)) * V_LD + (c % (D / 8)) * 8] = vreg[i];
-    }
-  };
+  for (int dc = 0; dc < DC; ++dc) k_off[dc] = L::off(ql, 2 * dc + hh);
   auto compute_s = [&](int buf, f32x16 (&s)[KT]) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       s[kt] = f32x16{};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const u32x4 kf = *(const u32x4*)&Ks[buf][(kt * 32 + ql) * K_LD + dc * 16 + hh * 8];
+        const u32x4 kf = *(const u32x4*)&Ks[buf][kt * (32 / L::RPI) * L::GB + k_off[dc]];
         s[kt] = Mfma<T>::mma32(kf, qf[dc], s[kt]);
       }
     }
   };
 
-  f32x16 s_a[KT], s_b[KT];
-  if (ntiles > 0) {
-    load_k(0);
-    store_k(0);
-    if (ntiles > 1) load_k(1);
-    load_v(0);
-    __syncthreads();
-    if (w_tiles > 0) compute_s(0, s_a);
-  }
-
-  // V fragment addressing for ds_read_b64_tr_b16: in each 16-lane group,
-  // lane i reads key row (4*half + i/4) and d columns [16*dh + 4*(i%4), +4).
+  // V fragment (A of O^T) via ds_read_b64_tr_b16: in each 16-lane group,
+  // lane i reads row 4*hh + i/4 (+8 for the second half of the 16 keys) and
+  // the 4 columns at 32*dt + 16*dhalf + 4*(i%4).
   const int g16 = lane & 15;
   const int v_row = 4 * hh + (g16 >> 2);
   const int v_col = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+  int v_off[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int col = dt * 32 + v_col;
+    v_off[dt] = L::off(v_row, col / 8) + (col % 8) * 2;
+  }
+
+  f32x16 s_a[KT], s_b[KT];
+  if (ntiles > 0) {
+    load_tile(rk, Ks[0], 0);
+    load_tile(rk, Ks[1], 1);
+    load_tile(rv, Vs[0], 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (w_tiles > 0) compute_s(0, s_a);
+  }
 
   // One tile of the pipeline: S of tile j+1 into s_nxt, softmax and P V of
   // tile j from s_cur. FULL tiles (every row of every wave sees every key of
@@ -194,83 +217,89 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
   // general path with per-wave liveness and masking.
   auto tile = [&](int j, f32x16 (&s_cur)[KT], f32x16 (&s_nxt)[KT], auto full) {
     constexpr bool FULL = decltype(full)::value;
-    if (FULL || j + 1 < ntiles) store_k((j + 1) & 1);
-    store_v(j & 1);
+    // Every wave has finished tile j-1: the K buffer of tile j and the V
+    // buffer of tile j-1 are free. Loads past the last tile read inside the
+    // head, or zeros past the resource end, and are never used.
     __syncthreads();
-    // Loads past the last tile read inside the head (or as zeros past the
-    // resource end) and are never used.
-    if (FULL || j + 2 < ntiles) load_k(j + 2);
-    if (FULL || j + 1 < ntiles) load_v(j + 1);
+    if (FULL || j + 2 < ntiles) load_tile(rk, Ks[j & 1], j + 2);
+    if (FULL || j + 1 < ntiles) load_tile(rv, Vs[(j + 1) & 1], j + 1);
     const bool live = FULL || j < w_tiles;
-    if (!live) return;
+    if (live) {
+      if constexpr (!FULL) {
+        const int t0 = j * BC;
+        const bool need_mask = (t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0);
+        if (need_mask) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+              const bool vis = key < kv_end && (!a.causal || key <= my_q);
+              if (!vis) s_cur[kt][r] = -INFINITY;
+            }
+          }
+        }
+      }
 
-    if constexpr (!FULL) {
-      const int t0 = j * BC;
-      const bool need_mask = (t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0);
-      if (need_mask) {
+      float mx = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool vis = key < kv_end && (!a.causal || key <= my_q);
-            if (!vis) s_cur[kt][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
+      }
+      mx = fmaxf(mx, swap_halves(mx));
+      if (__any(mx > m_ref)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_new == m_ref) ? 1.f : fast_exp2((m_ref - m_new) * sl2);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_ref = m_new;
+      }
+
+      if (FULL || j + 1 < w_tiles) compute_s((j + 1) & 1, s_nxt);
+
+      const float mref2 = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s_cur[kt][r], sl2, -mref2));
+          s_cur[kt][r] = p;
+          lsum += p;
+        }
+      }
+      l_run += lsum;
+
+      // O^T += V^T P^T, 16 keys per MFMA. Rows kt*32 + c2*16 (+8) of the V
+      // tile start whole groups, so they only move the group base.
+      const unsigned char* vb = Vs[j & 1];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const u32x4 pf = {Mfma<T>::pack(s_cur[kt][8 * c2 + 0], s_cur[kt][8 * c2 + 1]),
+                            Mfma<T>::pack(s_cur[kt][8 * c2 + 2], s_cur[kt][8 * c2 + 3]),
+                            Mfma<T>::pack(s_cur[kt][8 * c2 + 4], s_cur[kt][8 * c2 + 5]),
+                            Mfma<T>::pack(s_cur[kt][8 * c2 + 6], s_cur[kt][8 * c2 + 7])};
+          constexpr int kGroupsPer8 = 8 / L::RPI;  // groups spanned by 8 rows (0 if within one)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int row0 = kt * 32 + c2 * 16;
+            const unsigned char* vp = vb + (row0 / L::RPI) * L::GB + v_off[dt];
+            const u32x2 v0 = lds_read_tr((const uint16_t*)vp);
+            const u32x2 v1 = lds_read_tr(
+                (const uint16_t*)(vp + (kGroupsPer8 ? kGroupsPer8 * L::GB : 8 * L::RB)));
+            const u32x4 vf = {v0.x, v0.y, v1.x, v1.y};
+            oacc[dt] = Mfma<T>::mma32(vf, pf, oacc[dt]);
           }
         }
       }
     }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
-    }
-    mx = fmaxf(mx, swap_halves(mx));
-    if (__any(mx > m_ref)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = (m_new == m_ref) ? 1.f : fast_exp2((m_ref - m_new) * sl2);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      m_ref = m_new;
-    }
-
-    if (FULL || j + 1 < w_tiles) compute_s((j + 1) & 1, s_nxt);
-
-    const float mref2 = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
-    float lsum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s_cur[kt][r], sl2, -mref2));
-        s_cur[kt][r] = p;
-        lsum += p;
-      }
-    }
-    l_run += lsum;
-
-    // O^T += V^T P^T, 16 keys per MFMA.
-    const uint16_t* vb = &Vs[j & 1][v_row * V_LD + v_col];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const u32x4 pf = {Mfma<T>::pack(s_cur[kt][8 * c2 + 0], s_cur[kt][8 * c2 + 1]),
-                          Mfma<T>::pack(s_cur[kt][8 * c2 + 2], s_cur[kt][8 * c2 + 3]),
-                          Mfma<T>::pack(s_cur[kt][8 * c2 + 4], s_cur[kt][8 * c2 + 5]),
-                          Mfma<T>::pack(s_cur[kt][8 * c2 + 6], s_cur[kt][8 * c2 + 7])};
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t* vp = vb + (kt * 32 + c2 * 16) * V_LD + dt * 32;
-          const u32x2 v0 = lds_read_tr(vp);
-          const u32x2 v1 = lds_read_tr(vp + 8 * V_LD);
-          const u32x4 vf = {v0.x, v0.y, v1.x, v1.y};
-          oacc[dt] = Mfma<T>::mma32(vf, pf, oacc[dt]);
-        }
-      }
-    }
+    // This wave's loads for the next tiles must have landed before anyone
+    // passes the next barrier.
+    __builtin_amdgcn_s_waitcnt(0);
   };
 
   using Full = std::integral_constant<bool, true>;
