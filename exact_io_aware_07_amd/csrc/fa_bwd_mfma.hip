@@ -14,13 +14,16 @@
 // Three launches, no atomics, so the result is bit-reproducible:
 //   1. dsum_kernel:  D_i = rowsum(dO * O) into the caller's workspace.
 //   2. dkdv_kernel:  one workgroup per key block; K and V stay in VGPRs, the
-//      loop streams query tiles (Q, dO, LSE, D) through LDS. Per tile:
-//      S = Q K^T and dP = dO V^T with the key as the accumulator column (lane),
-//      so P and dS come out of the accumulator already in the layout the
-//      next two products take as B operand: dV^T += dO^T P, dK^T += Q^T dS.
+//      loop streams query tiles (Q, dO from HBM straight into LDS; LSE, D)
+//      past them. Per tile: S = Q K^T and dP = dO V^T with the key as the
+//      accumulator column (lane), so P and dS come out of the accumulator
+//      already in the layout the next two products take as B operand:
+//      dV^T += dO^T P, dK^T += Q^T dS, whose A operands (dO^T, Q^T) are
+//      transposed reads (ds_read_b64_tr_b16) of the same row-major tiles.
 //   3. dq_kernel: one workgroup per query block; Q and dO stay in VGPRs, the
 //      loop streams key tiles (K, V) through LDS. Per tile: S^T = K Q^T and
-//      dP^T = V dO^T with the query as the lane, then dQ^T += K^T dS^T.
+//      dP^T = V dO^T with the query as the lane, then dQ^T += K^T dS^T with
+//      K^T a transposed read of the K tile.
 // Kernel 3 recomputes S and dP, so the MFMA work is 7 products per tile pair
 // against the 5 the gradients need.
 #include "fa_internal.h"
@@ -54,79 +57,39 @@ __global__ __launch_bounds__(256) void dsum_kernel(const uint16_t* __restrict__ 
   if (row < rows && part == 0) dsum[row] = acc;
 }
 
-// Load 4 consecutive rows x 8 columns (16 bytes per row) of a [N, D] tile.
-template <int D>
-__device__ inline void load_unit(const uint16_t* __restrict__ base, int row0, int c8, int valid,
-                                 u32x4 (&r)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (row0 + i < valid) ? *(const u32x4*)(base + (size_t)(row0 + i) * D + c8 * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-// Store a 4x8 unit row-major (stride RLD) at (row0, 8*c8).
-__device__ inline void store_rows(uint16_t* dst, int RLD, int row0, int c8, const u32x4 (&r)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *(u32x4*)&dst[(row0 + i) * RLD + c8 * 8] = r[i];
-}
-
-// Store a 4x8 unit transposed: for each of the 8 columns, the 4 rows as one
-// 8-byte run at [col][row0 .. row0+3] (stride TLD).
-__device__ inline void store_cols(uint16_t* dst, int TLD, int row0, int c8, const u32x4 (&r)[4]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t w0 = r[0][p], w1 = r[1][p], w2 = r[2][p], w3 = r[3][p];
-    const u32x2 lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-    const u32x2 hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-    *(u32x2*)&dst[(c8 * 8 + 2 * p) * TLD + row0] = lo;
-    *(u32x2*)&dst[(c8 * 8 + 2 * p + 1) * TLD + row0] = hi;
-  }
-}
-
-// A fragment from a transposed tile: row `m` of the transpose, 16 reduction
-// indices starting at k0, taken as runs [k0+4h, +4) and [k0+8+4h, +4) — the
-// order in which a 32x32 accumulator holds them in lane half h.
-__device__ inline u32x4 frag_cols(const uint16_t* src, int TLD, int m, int k0, int hh) {
-  const uint16_t* p = &src[m * TLD + k0 + 4 * hh];
-  const u32x2 a = *(const u32x2*)p;
-  const u32x2 b = *(const u32x2*)(p + 8);
-  return u32x4{a.x, a.y, b.x, b.y};
-}
-
 template <typename T>
 __device__ inline u32x4 pack8(const f32x16& x, int base) {
   return u32x4{Mfma<T>::pack(x[base + 0], x[base + 1]), Mfma<T>::pack(x[base + 2], x[base + 3]),
                Mfma<T>::pack(x[base + 4], x[base + 5]), Mfma<T>::pack(x[base + 6], x[base + 7])};
 }
 
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (b, h, key block of 32 * WA keys).
+// dK, dV: one workgroup per (b, h, key block of 128 keys); wave w owns keys
+// [32w, 32w + 32) with their K and V rows in VGPRs. Query tiles of BQ rows
+// (Q, dO straight from HBM into LDS, LSE and D through VGPRs) stream past.
 template <int D>
 struct DkdvCfg {
-  static constexpr int WA = (D == 128) ? 4 : 4;
-  static constexpr int MINB = (D == 128) ? 1 : 2;
+  static constexpr int BQ = 64;                  // queries per tile
+  static constexpr int MINW = (D == 128) ? 1 : 2;  // waves per SIMD the registers allow
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(64 * DkdvCfg<D>::WA, DkdvCfg<D>::MINB) void dkdv_kernel(BwdArgs a) {
-  constexpr int WA = DkdvCfg<D>::WA;
-  constexpr int NT = 64 * WA;
-  constexpr int BK = 32 * WA;  // keys per workgroup
-  constexpr int BQ = 32;       // queries per tile
+__global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(BwdArgs a) {
+  using L = TileLayout<D>;
+  constexpr int BK = 32 * kBwdWaves;  // keys per workgroup
+  constexpr int BQ = DkdvCfg<D>::BQ;
+  constexpr int QS = BQ / 32;         // 32-query sub-tiles
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
-  constexpr int RLD = D + 8;   // row-major tile stride (u16)
-  constexpr int TLD = BQ + 4;  // transposed tile stride (u16)
-  constexpr int UPT = (BQ / 4) * (D / 8);  // 4x8 units per tensor per tile
-  static_assert(2 * UPT <= NT, "one unit per thread at most");
+  constexpr int TB = L::bytes(BQ);
 
-  __shared__ __attribute__((aligned(16))) uint16_t Qr[2][BQ * RLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Gr[2][BQ * RLD];  // dO rows
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Gt[2][D * TLD];
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];  // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];  // D_i
+  __shared__ __attribute__((aligned(1024))) unsigned char Qs[2][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Gs[2][TB];  // dO
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];            // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];            // D_i
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -138,29 +101,29 @@ __global__ __launch_bounds__(64 * DkdvCfg<D>::WA, DkdvCfg<D>::MINB) void dkdv_ke
   const int nkb = (N + BK - 1) / BK;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nkb;
-  const int kb = logical % nkb;  // causal: key block 0 has the most work, and runs first
+  const int kb = logical % nkb;  // causal: key block 0 has the most work and runs first
   const int b = bh / a.H;
 
   const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + head_off;
-  const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + head_off;
-  const uint16_t* __restrict__ Vg = (const uint16_t*)a.v + head_off;
-  const uint16_t* __restrict__ Gg = (const uint16_t*)a.dout + head_off;
   const float* __restrict__ Lg = a.lse + (size_t)bh * N;
   const float* __restrict__ Dg = a.dsum + (size_t)bh * N;
-
   int kv_end = N;
   if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint16_t*)a.dout + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + head_off, (uint32_t)kv_end * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + head_off, (uint32_t)kv_end * D * 2);
 
   const int key0 = kb * BK + wave * 32;
   const int my_key = key0 + kl;
 
+  // B operands of S = Q K^T and dP = dO V^T: this lane's key row, 8 d
+  // elements per 16-wide chunk. Keys at or past kv_end read as zero.
   u32x4 kf[DC], vf[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) {
-    const bool ok = my_key < kv_end;
-    kf[dc] = ok ? *(const u32x4*)(Kg + (size_t)my_key * D + dc * 16 + hh * 8) : u32x4{0u, 0u, 0u, 0u};
-    vf[dc] = ok ? *(const u32x4*)(Vg + (size_t)my_key * D + dc * 16 + hh * 8) : u32x4{0u, 0u, 0u, 0u};
+    kf[dc] = buf_load16(rk, (uint32_t)(my_key * D + dc * 16 + hh * 8) * 2);
+    vf[dc] = buf_load16(rv, (uint32_t)(my_key * D + dc * 16 + hh * 8) * 2);
   }
 
   f32x16 dk[DT], dv[DT];
@@ -170,101 +133,109 @@ __global__ __launch_bounds__(64 * DkdvCfg<D>::WA, DkdvCfg<D>::MINB) void dkdv_ke
     dv[dt] = f32x16{};
   }
 
-  // Query tiles this key block can contribute to.
   const int blk_key0 = kb * BK;
-  const bool any_key = blk_key0 < kv_end;
   const int qt_begin = (a.causal ? blk_key0 : 0) / BQ;
-  const int qt_end = any_key ? (N + BQ - 1) / BQ : qt_begin;
+  const int qt_end = (blk_key0 < kv_end) ? (N + BQ - 1) / BQ : qt_begin;
   const float sl2 = a.scale * kLog2e;
 
-  // Prefetch registers: one 4x8 unit of Q or dO per thread, plus LSE/D.
-  u32x4 ureg[4];
-  float sreg = 0.f;
-  const bool unit_thread = tid < 2 * UPT;
-  const int ut = tid % UPT;
-  const int ug = ut % (BQ / 4);
-  const int uc8 = ut / (BQ / 4);
-  const uint16_t* usrc = (tid < UPT) ? Qg : Gg;
+  // Row-major fragment reads (A of S and dP): row qs*32 + kl, chunk 2dc + hh.
+  int r_off[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) r_off[dc] = L::off(kl, 2 * dc + hh);
+  // Transposed fragment reads (A of dV^T and dK^T): 16 queries x 32 d.
+  int t_off[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  auto load_tile = [&](int it) {
-    const int q0 = it * BQ;
-    if (unit_thread) load_unit<D>(usrc, q0 + 4 * ug, uc8, N, ureg);
+  // LSE (pre-scaled by log2 e) and D of a query tile go through one VGPR of
+  // the first 2*BQ threads. A row without any visible key (LSE = -inf) has
+  // all its probabilities masked; a finite stand-in avoids inf - inf.
+  float sreg = 0.f;
+  auto load_stats = [&](int it) {
     if (tid < 2 * BQ) {
-      const int q = q0 + (tid % BQ);
+      const int q = it * BQ + (tid % BQ);
       float x = 0.f;
       if (q < N) x = (tid < BQ) ? Lg[q] * kLog2e : Dg[q];
-      // rows without any visible key carry LSE = -inf; their P is masked to
-      // zero, so a finite stand-in avoids inf - inf.
       sreg = (x == -INFINITY) ? 0.f : x;
     }
   };
-  auto store_tile = [&](int buf) {
-    if (unit_thread) {
-      uint16_t* rdst = (tid < UPT) ? Qr[buf] : Gr[buf];
-      uint16_t* tdst = (tid < UPT) ? Qt[buf] : Gt[buf];
-      store_rows(rdst, RLD, 4 * ug, uc8, ureg);
-      store_cols(tdst, TLD, 4 * ug, uc8, ureg);
-    }
-    if (tid < 2 * BQ) {
-      if (tid < BQ) Ls[buf][tid] = sreg;
-      else Ds[buf][tid - BQ] = sreg;
-    }
+  auto store_stats = [&](int buf) {
+    if (tid < BQ) Ls[buf][tid] = sreg;
+    else if (tid < 2 * BQ) Ds[buf][tid - BQ] = sreg;
+  };
+  auto load_tiles = [&](int it, int buf) {
+    load_tile_lds<D, BQ, kBwdWaves>(rq, Qs[buf], it * BQ, wave, lane);
+    load_tile_lds<D, BQ, kBwdWaves>(rg, Gs[buf], it * BQ, wave, lane);
   };
 
-  if (qt_begin < qt_end) load_tile(qt_begin);
+  if (qt_begin < qt_end) {
+    load_tiles(qt_begin, 0);
+    load_stats(qt_begin);
+    store_stats(0);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   for (int it = qt_begin; it < qt_end; ++it) {
     const int buf = (it - qt_begin) & 1;
-    store_tile(buf);
+    // Tile it has landed everywhere; every wave is done with tile it-1, so
+    // the other buffers are free for tile it+1.
     __syncthreads();
-    if (it + 1 < qt_end) load_tile(it + 1);
+    const bool more = it + 1 < qt_end;
+    if (more) {
+      load_tiles(it + 1, buf ^ 1);
+      load_stats(it + 1);
+    }
 
     const int q0 = it * BQ;
-    // Skip tiles wholly before this wave's first key (causal) or past its keys.
-    const bool wave_live = (key0 < kv_end) && (!a.causal || q0 + BQ - 1 >= key0);
-    if (wave_live) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const u32x4 qa = *(const u32x4*)&Qr[buf][kl * RLD + dc * 16 + hh * 8];
-        s = Mfma<T>::mma32(qa, kf[dc], s);
-      }
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const u32x4 ga = *(const u32x4*)&Gr[buf][kl * RLD + dc * 16 + hh * 8];
-        dp = Mfma<T>::mma32(ga, vf[dc], dp);
-      }
+    const bool live = (key0 < kv_end) && (!a.causal || q0 + BQ - 1 >= key0);
+    if (live) {
       const bool need_mask = (q0 + BQ > N) || (key0 + 32 > kv_end) || (a.causal && key0 + 31 > q0);
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qi = 8 * r4 + 4 * hh;
-        const f32x4 l4 = *(const f32x4*)&Ls[buf][qi];
-        const f32x4 d4 = *(const f32x4*)&Ds[buf][qi];
+      for (int qs = 0; qs < QS; ++qs) {
+        const unsigned char* qt = Qs[buf] + qs * (32 / L::RPI) * L::GB;
+        const unsigned char* gt = Gs[buf] + qs * (32 / L::RPI) * L::GB;
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
-          if (need_mask) {
-            const int q = q0 + qi + e;
-            const bool vis = (q < N) && (my_key < kv_end) && (!a.causal || my_key <= q);
-            p = vis ? p : 0.f;
+        for (int dc = 0; dc < DC; ++dc) s = Mfma<T>::mma32(*(const u32x4*)(qt + r_off[dc]), kf[dc], s);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) dp = Mfma<T>::mma32(*(const u32x4*)(gt + r_off[dc]), vf[dc], dp);
+        // lane = key; register r holds query qs*32 + 8(r/4) + 4hh + r%4
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qi = qs * 32 + 8 * r4 + 4 * hh;
+          const f32x4 l4 = *(const f32x4*)&Ls[buf][qi];
+          const f32x4 d4 = *(const f32x4*)&Ds[buf][qi];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
+            if (need_mask) {
+              const int q = q0 + qi + e;
+              const bool vis = (q < N) && (my_key < kv_end) && (!a.causal || my_key <= q);
+              p = vis ? p : 0.f;
+            }
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[e]);
           }
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[e]);
         }
-      }
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const u32x4 pf = pack8<T>(s, 8 * c2);
-        const u32x4 sf = pack8<T>(dp, 8 * c2);
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const u32x4 pf = pack8<T>(s, 8 * c2);
+          const u32x4 sf = pack8<T>(dp, 8 * c2);
+          const int rb = (2 * qs + c2) * L::rows16();
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const u32x4 ga = frag_cols(Gt[buf], TLD, dt * 32 + kl, 16 * c2, hh);
-          dv[dt] = Mfma<T>::mma32(ga, pf, dv[dt]);
-          const u32x4 qa = frag_cols(Qt[buf], TLD, dt * 32 + kl, 16 * c2, hh);
-          dk[dt] = Mfma<T>::mma32(qa, sf, dk[dt]);
+          for (int dt = 0; dt < DT; ++dt) {
+            const unsigned char* gp = Gs[buf] + rb + t_off[dt];
+            const u32x2 g0 = lds_read_tr(gp), g1 = lds_read_tr(gp + L::half_step());
+            dv[dt] = Mfma<T>::mma32(u32x4{g0.x, g0.y, g1.x, g1.y}, pf, dv[dt]);
+            const unsigned char* qp = Qs[buf] + rb + t_off[dt];
+            const u32x2 q0v = lds_read_tr(qp), q1v = lds_read_tr(qp + L::half_step());
+            dk[dt] = Mfma<T>::mma32(u32x4{q0v.x, q0v.y, q1v.x, q1v.y}, sf, dk[dt]);
+          }
         }
       }
     }
+    if (more) store_stats(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // dK^T / dV^T accumulators: lane = key, registers = d in runs of 4.
@@ -288,28 +259,27 @@ __global__ __launch_bounds__(64 * DkdvCfg<D>::WA, DkdvCfg<D>::MINB) void dkdv_ke
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per (b, h, query block of 128 rows).
+// dQ: one workgroup per (b, h, query block of 128 rows); wave w owns rows
+// [32w, 32w + 32) with its Q and dO rows in VGPRs. Key tiles of BC keys (K,
+// V straight from HBM into LDS) stream past; K is read both row-wise (A of
+// S^T) and transposed (A of dQ^T).
 template <int D>
 struct DqCfg {
-  static constexpr int BC = (D == 128) ? 32 : 64;  // keys per tile
+  static constexpr int BC = 64;  // keys per tile
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
-  constexpr int NT = 256;
-  constexpr int BR = 128;
+__global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
+  using L = TileLayout<D>;
+  constexpr int BR = 32 * kBwdWaves;
   constexpr int BC = DqCfg<D>::BC;
   constexpr int KT = BC / 32;
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
-  constexpr int RLD = D + 8;
-  constexpr int TLD = BC + 4;
-  constexpr int UPT = (BC / 4) * (D / 8);
-  static_assert(2 * UPT == NT, "one unit of K or V per thread");
+  constexpr int TB = L::bytes(BC);
 
-  __shared__ __attribute__((aligned(16))) uint16_t Kr[2][BC * RLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vr[2][BC * RLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TLD];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -326,13 +296,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   const int b = bh / a.H;
 
   const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* __restrict__ Qg = (const uint16_t*)a.q + head_off;
-  const uint16_t* __restrict__ Kg = (const uint16_t*)a.k + head_off;
-  const uint16_t* __restrict__ Vg = (const uint16_t*)a.v + head_off;
-  const uint16_t* __restrict__ Gg = (const uint16_t*)a.dout + head_off;
-
   int kv_end = N;
   if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint16_t*)a.dout + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + head_off, (uint32_t)kv_end * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + head_off, (uint32_t)kv_end * D * 2);
+
   const int q_blk0 = qb * BR;
   int kv_lim = kv_end;
   if (a.causal) kv_lim = min(kv_lim, min(q_blk0 + BR, N));
@@ -346,9 +316,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   u32x4 qf[DC], gf[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) {
-    const bool ok = my_q < N;
-    qf[dc] = ok ? *(const u32x4*)(Qg + (size_t)my_q * D + dc * 16 + hh * 8) : u32x4{0u, 0u, 0u, 0u};
-    gf[dc] = ok ? *(const u32x4*)(Gg + (size_t)my_q * D + dc * 16 + hh * 8) : u32x4{0u, 0u, 0u, 0u};
+    qf[dc] = buf_load16(rq, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
+    gf[dc] = buf_load16(rg, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
   }
   float lse2 = 0.f, dsum = 0.f;
   if (my_q < N) {
@@ -362,49 +331,44 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
 
-  u32x4 ureg[4];
-  const int ut = tid % UPT;
-  const int ug = ut % (BC / 4);
-  const int uc8 = ut / (BC / 4);
-  const bool is_k = tid < UPT;
-  const uint16_t* usrc = is_k ? Kg : Vg;
+  int r_off[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) r_off[dc] = L::off(ql, 2 * dc + hh);
+  int t_off[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  auto load_tile = [&](int j) { load_unit<D>(usrc, j * BC + 4 * ug, uc8, kv_end, ureg); };
-  auto store_tile = [&](int buf) {
-    if (is_k) {
-      store_rows(Kr[buf], RLD, 4 * ug, uc8, ureg);
-      store_cols(Kt[buf], TLD, 4 * ug, uc8, ureg);
-    } else {
-      store_rows(Vr[buf], RLD, 4 * ug, uc8, ureg);
-    }
+  auto load_tiles = [&](int j, int buf) {
+    load_tile_lds<D, BC, kBwdWaves>(rk, Ks[buf], j * BC, wave, lane);
+    load_tile_lds<D, BC, kBwdWaves>(rv, Vs[buf], j * BC, wave, lane);
   };
 
-  if (ntiles > 0) load_tile(0);
+  if (ntiles > 0) {
+    load_tiles(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
-    store_tile(buf);
     __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1);
+    if (j + 1 < ntiles) load_tiles(j + 1, buf ^ 1);
 
     const int t0 = j * BC;
     if (t0 < w_lim) {
       f32x16 s[KT], dp[KT];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
+        const unsigned char* kt_p = Ks[buf] + kt * (32 / L::RPI) * L::GB;
+        const unsigned char* vt_p = Vs[buf] + kt * (32 / L::RPI) * L::GB;
         s[kt] = f32x16{};
         dp[kt] = f32x16{};
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const u32x4 ka = *(const u32x4*)&Kr[buf][(kt * 32 + ql) * RLD + dc * 16 + hh * 8];
-          s[kt] = Mfma<T>::mma32(ka, qf[dc], s[kt]);
-        }
+        for (int dc = 0; dc < DC; ++dc)
+          s[kt] = Mfma<T>::mma32(*(const u32x4*)(kt_p + r_off[dc]), qf[dc], s[kt]);
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const u32x4 va = *(const u32x4*)&Vr[buf][(kt * 32 + ql) * RLD + dc * 16 + hh * 8];
-          dp[kt] = Mfma<T>::mma32(va, gf[dc], dp[kt]);
-        }
+        for (int dc = 0; dc < DC; ++dc)
+          dp[kt] = Mfma<T>::mma32(*(const u32x4*)(vt_p + r_off[dc]), gf[dc], dp[kt]);
       }
-      const bool need_mask = (t0 + BC > kv_end) || (my_q >= N) || (a.causal && t0 + BC - 1 > wq0);
+      const bool need_mask = (t0 + BC > kv_end) || (wq0 + 32 > N) || (a.causal && t0 + BC - 1 > wq0);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -423,14 +387,17 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           const u32x4 sf = pack8<T>(dp[kt], 8 * c2);
+          const int rb = (2 * kt + c2) * L::rows16();
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const u32x4 ka = frag_cols(Kt[buf], TLD, dt * 32 + ql, kt * 32 + 16 * c2, hh);
-            dq[dt] = Mfma<T>::mma32(ka, sf, dq[dt]);
+            const unsigned char* kp = Ks[buf] + rb + t_off[dt];
+            const u32x2 k0 = lds_read_tr(kp), k1 = lds_read_tr(kp + L::half_step());
+            dq[dt] = Mfma<T>::mma32(u32x4{k0.x, k0.y, k1.x, k1.y}, sf, dq[dt]);
           }
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   if (my_q < N) {
@@ -459,16 +426,15 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & (int)BwdStage::DKDV) {
-    constexpr int WA = DkdvCfg<D>::WA;
-    const long nkb = (a.N + 32 * WA - 1) / (32 * WA);
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nkb)), dim3(64 * WA),
-                       0, st, a);
+    const long nkb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nkb)),
+                       dim3(kBwdThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & (int)BwdStage::DQ) {
-    const long nqb = (a.N + 127) / 128;
-    hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nqb)), dim3(256), 0, st,
-                       a);
+    const long nqb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+    hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nqb)),
+                       dim3(kBwdThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return e;

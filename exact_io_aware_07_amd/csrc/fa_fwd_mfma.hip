@@ -59,40 +59,6 @@ struct FwdTile {
   static constexpr int BC = 64;  // keys per tile
 };
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
-}
-
-// 4 x 16-bit from LDS, transposed across each group of 16 lanes.
-__device__ inline u32x2 lds_read_tr(const uint16_t* p) {
-  typedef short i16x4 __attribute__((ext_vector_type(4)));
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) void*)p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-// LDS tile layout for direct loads: [rows][D] bf16/fp16, in groups of RPI
-// rows (1 KiB, one load instruction), each group padded by 16 bytes; within
-// a group, logical 16-byte chunk c of row r' sits at position c ^ sw(r').
-template <int D>
-struct TileLayout {
-  static constexpr int RB = D * 2;            // bytes per row
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int RPI = 1024 / RB;       // rows per 1 KiB group
-  static constexpr int GB = 1024 + 16;        // bytes per group incl. pad
-  __device__ static constexpr int sw(int r) { return D == 128 ? 4 * r : 2 * (r >> 1); }
-  // byte offset of logical (row, chunk) inside a tile
-  __device__ static constexpr int off(int row, int chunk) {
-    return (row / RPI) * GB + (row % RPI) * RB + ((chunk ^ sw(row % RPI)) << 4);
-  }
-  static constexpr int bytes(int rows) { return rows / RPI * GB; }
-};
-
 template <typename T, int D, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(FwdArgs a) {
   using L = TileLayout<D>;
@@ -101,8 +67,6 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
   constexpr int DC = D / 16;                    // 16-wide d chunks (S reduction)
   constexpr int DT = D / 32;                    // 32-wide d tiles of O^T
   constexpr int TB = L::bytes(BC);              // bytes per K or V tile
-  constexpr int GPW = BC / L::RPI / kWaves;     // load instructions per wave per tile
-  static_assert(GPW >= 1 && BC % (L::RPI * kWaves) == 0, "tile too small for the workgroup");
 
   __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TB];
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TB];
@@ -151,20 +115,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
   float l_run = 0.f;        // running sum over this half's keys, against m_ref
   const float sl2 = a.scale * kLog2e;
 
-  // Direct loads: lane l of a wave's instruction for group G fills position
-  // l of the group (row l / CPR, position l % CPR) with the logical chunk
-  // (l % CPR) ^ sw(row) of that row.
-  const int ld_row = lane / L::CPR;
-  const int ld_chunk = (lane % L::CPR) ^ L::sw(ld_row);
   auto load_tile = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int j) {
-#pragma unroll
-    for (int g = 0; g < GPW; ++g) {
-      const int G = wave * GPW + g;
-      const int row = j * BC + G * L::RPI + ld_row;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(dst + G * L::GB), 16,
-          (row * D + ld_chunk * 8) * 2, 0, 0, 0);
-    }
+    load_tile_lds<D, BC, kWaves>(r, dst, j * BC, wave, lane);
   };
 
   // K fragment (A of S^T): row kt*32 + ql, chunk 2*dc + hh. The row's place
@@ -185,18 +137,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
     }
   };
 
-  // V fragment (A of O^T) via ds_read_b64_tr_b16: in each 16-lane group,
-  // lane i reads row 4*hh + i/4 (+8 for the second half of the 16 keys) and
-  // the 4 columns at 32*dt + 16*dhalf + 4*(i%4).
-  const int g16 = lane & 15;
-  const int v_row = 4 * hh + (g16 >> 2);
-  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+  // V fragment (A of O^T) via ds_read_b64_tr_b16 over the 16 keys x 32 d
+  // block at rows kt*32 + c2*16, columns dt*32.
   int v_off[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int col = dt * 32 + v_col;
-    v_off[dt] = L::off(v_row, col / 8) + (col % 8) * 2;
-  }
+  for (int dt = 0; dt < DT; ++dt) v_off[dt] = L::tr_off(lane, dt * 32);
 
   f32x16 s_a[KT], s_b[KT];
   if (ntiles > 0) {
@@ -283,14 +228,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
                             Mfma<T>::pack(s_cur[kt][8 * c2 + 2], s_cur[kt][8 * c2 + 3]),
                             Mfma<T>::pack(s_cur[kt][8 * c2 + 4], s_cur[kt][8 * c2 + 5]),
                             Mfma<T>::pack(s_cur[kt][8 * c2 + 6], s_cur[kt][8 * c2 + 7])};
-          constexpr int kGroupsPer8 = 8 / L::RPI;  // groups spanned by 8 rows (0 if within one)
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int row0 = kt * 32 + c2 * 16;
-            const unsigned char* vp = vb + (row0 / L::RPI) * L::GB + v_off[dt];
-            const u32x2 v0 = lds_read_tr((const uint16_t*)vp);
-            const u32x2 v1 = lds_read_tr(
-                (const uint16_t*)(vp + (kGroupsPer8 ? kGroupsPer8 * L::GB : 8 * L::RB)));
+            const unsigned char* vp = vb + (2 * kt + c2) * L::rows16() + v_off[dt];
+            const u32x2 v0 = lds_read_tr(vp);
+            const u32x2 v1 = lds_read_tr(vp + L::half_step());
             const u32x4 vf = {v0.x, v0.y, v1.x, v1.y};
             oacc[dt] = Mfma<T>::mma32(vf, pf, oacc[dt]);
           }

@@ -116,6 +116,88 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 // Value of lane (l ^ 32): the other half of the wave.
 __device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// Buffer resource over [base, base + bytes): loads at or past the end read
+// as zero, which is how every kernel here pads ragged tiles.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i supplies an 8-byte
+// row M[i] (4 x 16-bit) and lane 4a + b receives M[a][b], M[a+4][b],
+// M[a+8][b], M[a+12][b]. Pointed at a 4-row x 16-column block of a
+// row-major tile (lane i at row i / 4, columns 4 * (i % 4) .. +3), every
+// lane gets the 4 rows of its own column: a transposed fragment.
+__device__ inline u32x2 lds_read_tr(const void* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) void*)p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// LDS layout of a [rows][D] 16-bit tile filled by direct loads: groups of
+// RPI rows (1 KiB, one buffer_load ... lds per wave), each group padded by
+// 16 bytes; inside a group, logical 16-byte chunk c of row r' sits at
+// position c ^ sw(r'). For D = 128 (4 rows per group) sw = 4 r'; for D = 64
+// (8 rows) sw = 2 (r' / 2). With the pad, 16 lanes reading one chunk of 16
+// consecutive rows, and 16 lanes reading two adjacent chunks of 4
+// consecutive rows (the transposed-read pattern), fall on distinct banks.
+template <int D>
+struct TileLayout {
+  static constexpr int RB = D * 2;       // bytes per row
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;  // rows per 1 KiB group
+  static constexpr int GB = 1024 + 16;   // bytes per group incl. pad
+  __device__ static constexpr int sw(int r) { return D == 128 ? 4 * r : 2 * (r >> 1); }
+  // byte offset of logical (row, chunk) inside a tile
+  __device__ static constexpr int off(int row, int chunk) {
+    return (row / RPI) * GB + (row % RPI) * RB + ((chunk ^ sw(row % RPI)) << 4);
+  }
+  static constexpr int bytes(int rows) { return rows / RPI * GB; }
+  // Byte offset, inside a tile, of the transposed-read address of `lane`
+  // for the 16 x 32 block at rows [0, 16) and columns [col0, col0 + 32):
+  // lanes 0-31 read rows 0-3, lanes 32-63 rows 4-7 (the second half of the
+  // block, rows 8-15, is this plus half_step()); columns col0 + 16 * ((lane
+  // >> 4) & 1) + 4 * (lane % 4).
+  __device__ static int tr_off(int lane, int col0) {
+    const int g16 = lane & 15;
+    const int row = 4 * (lane >> 5) + (g16 >> 2);
+    const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+    return off(row, col / 8) + (col % 8) * 2;
+  }
+  // offset from rows r to rows r + 8 (r a multiple of 8)
+  static constexpr int half_step() { return RPI <= 8 ? (8 / RPI) * GB : 8 * RB; }
+  // offset from rows r to rows r + 16 (r a multiple of 16)
+  static constexpr int rows16() { return (16 / RPI) * GB; }
+};
+
+// Each wave of a workgroup of `waves` fills its share of a [rows][D] tile:
+// rows [row0, row0 + rows) of the tensor behind `r` go to `dst` in the
+// TileLayout above. Lane l of the instruction for group G writes position
+// l of that group (row l / CPR, position l % CPR), so it loads logical chunk
+// (l % CPR) ^ sw(row).
+template <int D, int ROWS, int WAVES>
+__device__ inline void load_tile_lds(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int row0,
+                                     int wave, int lane) {
+  using L = TileLayout<D>;
+  constexpr int GPW = ROWS / L::RPI / WAVES;
+  static_assert(GPW >= 1 && ROWS % (L::RPI * WAVES) == 0, "tile too small for the workgroup");
+  const int ld_row = lane / L::CPR;
+  const int ld_chunk = (lane % L::CPR) ^ L::sw(ld_row);
+#pragma unroll
+  for (int g = 0; g < GPW; ++g) {
+    const int G = wave * GPW + g;
+    const int row = row0 + G * L::RPI + ld_row;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(dst + G * L::GB), 16,
+        (row * D + ld_chunk * 8) * 2, 0, 0, 0);
+  }
+}
+
 // Block index remap so that consecutive logical blocks run on the same XCD.
 // Workgroups are dealt round-robin to the 8 XCDs; logical block
 // x * per + i is placed on physical slot i * 8 + x. Blocks past the largest
