@@ -26,6 +26,8 @@
 //      K^T a transposed read of the K tile.
 // Kernel 3 recomputes S and dP, so the MFMA work is 7 products per tile pair
 // against the 5 the gradients need.
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -99,9 +101,9 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 
   const int N = a.N;
   const int nkb = (N + BK - 1) / BK;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nkb;
-  const int kb = logical % nkb;  // causal: key block 0 has the most work and runs first
+  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nkb, a.B * a.H, a.causal);
+  const int bh = pk.bh;
+  const int kb = pk.rank;  // causal: key block 0 sees every query and has the most work
   const int b = bh / a.H;
 
   const size_t head_off = (size_t)bh * N * D;
@@ -174,7 +176,14 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
     store_stats(0);
     __builtin_amdgcn_s_waitcnt(0);
   }
-  for (int it = qt_begin; it < qt_end; ++it) {
+
+  // One query tile. FULL tiles (every key of the workgroup visible to every
+  // query of the tile) run with no liveness test and no mask, so both query
+  // sub-tiles sit in one basic block. Queries past N need no mask anywhere:
+  // their Q and dO rows read as zero and their LSE and D as zero, so their P
+  // meets a zero dO row and their dS is zero.
+  auto tile = [&](int it, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     const int buf = (it - qt_begin) & 1;
     // Tile it has landed everywhere; every wave is done with tile it-1, so
     // the other buffers are free for tile it+1.
@@ -184,11 +193,10 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
       load_tiles(it + 1, buf ^ 1);
       load_stats(it + 1);
     }
-
     const int q0 = it * BQ;
-    const bool live = (key0 < kv_end) && (!a.causal || q0 + BQ - 1 >= key0);
+    const bool live = FULL || ((key0 < kv_end) && (!a.causal || q0 + BQ - 1 >= key0));
     if (live) {
-      const bool need_mask = (q0 + BQ > N) || (key0 + 32 > kv_end) || (a.causal && key0 + 31 > q0);
+      const bool need_mask = !FULL && ((key0 + 32 > kv_end) || (a.causal && key0 + 31 > q0));
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
         const unsigned char* qt = Qs[buf] + qs * (32 / L::RPI) * L::GB;
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
             float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
             if (need_mask) {
               const int q = q0 + qi + e;
-              const bool vis = (q < N) && (my_key < kv_end) && (!a.causal || my_key <= q);
+              const bool vis = (my_key < kv_end) && (!a.causal || my_key <= q);
               p = vis ? p : 0.f;
             }
             s[r] = p;
@@ -236,7 +244,17 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
     }
     if (more) store_stats(buf ^ 1);
     __builtin_amdgcn_s_waitcnt(0);
-  }
+  };
+
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
+  // Tiles from it_full on see every key of the block: the keys all lie below
+  // kv_end and (causal) the tile's first query is at or past the last key.
+  int it_full = qt_end;
+  if (blk_key0 + BK <= kv_end) it_full = a.causal ? max(qt_begin, (blk_key0 + BK - 1 + BQ - 1) / BQ) : qt_begin;
+  it_full = min(it_full, qt_end);
+  for (int it = qt_begin; it < it_full; ++it) tile(it, Part{});
+  for (int it = it_full; it < qt_end; ++it) tile(it, Full{});
 
   // dK^T / dV^T accumulators: lane = key, registers = d in runs of 4.
   if (my_key < N) {
@@ -262,23 +280,37 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 // dQ: one workgroup per (b, h, query block of 128 rows); wave w owns rows
 // [32w, 32w + 32) with its Q and dO rows in VGPRs. Key tiles of BC keys (K,
 // V straight from HBM into LDS) stream past; K is read both row-wise (A of
-// S^T) and transposed (A of dQ^T).
+// S^T) and transposed (A of dQ^T). At d = 64 the tiles are software
+// pipelined: S^T and dP^T of tile j+1 are computed in the same basic block
+// as dS and dQ of tile j, so K runs through three LDS buffers (tile j for
+// dQ, j+1 for S, j+2 loading) and V through two.
+//
+// Rows past N and keys past kv_len need no mask here: their Q/dO or K/V
+// rows read as zero, so their dS (or their K row) is zero and they add
+// nothing to dQ. Only the causal diagonal is masked.
 template <int D>
 struct DqCfg {
-  static constexpr int BC = 64;  // keys per tile
+  // d = 64: pipelined, 32-key tiles. d = 128: the pipeline's second set of
+  // S/dP registers would cost the second wave per SIMD, which is worth
+  // more, so tiles of 64 keys are computed one at a time.
+  static constexpr bool PIPE = (D == 64);
+  static constexpr int BC = PIPE ? 32 : 64;  // keys per tile
+  static constexpr int NKB = PIPE ? 3 : 2;   // K tile buffers
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
   using L = TileLayout<D>;
   constexpr int BR = 32 * kBwdWaves;
+  constexpr bool PIPE = DqCfg<D>::PIPE;
   constexpr int BC = DqCfg<D>::BC;
+  constexpr int NKB = DqCfg<D>::NKB;
   constexpr int KT = BC / 32;
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
   constexpr int TB = L::bytes(BC);
 
-  __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks[NKB][TB];
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TB];
 
   const int tid = threadIdx.x;
@@ -289,10 +321,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
 
   const int N = a.N;
   const int nqb = (N + BR - 1) / BR;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nqb;
-  int qb = logical % nqb;
-  if (a.causal) qb = nqb - 1 - qb;
+  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nqb, a.B * a.H, a.causal);
+  const int bh = pk.bh;
+  const int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;
   const int b = bh / a.H;
 
   const size_t head_off = (size_t)bh * N * D;
@@ -312,6 +343,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
   const int my_q = wq0 + ql;
   int w_lim = kv_end;
   if (a.causal) w_lim = min(w_lim, min(wq0 + 31, N - 1) + 1);
+  const int w_tiles = (w_lim + BC - 1) / BC;
 
   u32x4 qf[DC], gf[DC];
 #pragma unroll
@@ -338,59 +370,80 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  auto load_tiles = [&](int j, int buf) {
-    load_tile_lds<D, BC, kBwdWaves>(rk, Ks[buf], j * BC, wave, lane);
-    load_tile_lds<D, BC, kBwdWaves>(rv, Vs[buf], j * BC, wave, lane);
+  auto load_k = [&](int j) { load_tile_lds<D, BC, kBwdWaves>(rk, Ks[j % NKB], j * BC, wave, lane); };
+  auto load_v = [&](int j) { load_tile_lds<D, BC, kBwdWaves>(rv, Vs[j & 1], j * BC, wave, lane); };
+  auto compute_sdp = [&](int j, f32x16 (&s)[KT], f32x16 (&dp)[KT]) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const unsigned char* kp = Ks[j % NKB] + kt * (32 / L::RPI) * L::GB;
+      const unsigned char* vp = Vs[j & 1] + kt * (32 / L::RPI) * L::GB;
+      s[kt] = f32x16{};
+      dp[kt] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) s[kt] = Mfma<T>::mma32(*(const u32x4*)(kp + r_off[dc]), qf[dc], s[kt]);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) dp[kt] = Mfma<T>::mma32(*(const u32x4*)(vp + r_off[dc]), gf[dc], dp[kt]);
+    }
   };
 
+  f32x16 s_a[KT], s_b[KT], p_a[KT], p_b[KT];
   if (ntiles > 0) {
-    load_tiles(0, 0);
+    load_k(0);
+    load_v(0);
+    if (PIPE && ntiles > 1) {
+      load_k(1);
+      load_v(1);
+    }
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (PIPE) {
+      __syncthreads();
+      if (w_tiles > 0) compute_sdp(0, s_a, p_a);
+    }
   }
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    __syncthreads();
-    if (j + 1 < ntiles) load_tiles(j + 1, buf ^ 1);
 
-    const int t0 = j * BC;
-    if (t0 < w_lim) {
-      f32x16 s[KT], dp[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const unsigned char* kt_p = Ks[buf] + kt * (32 / L::RPI) * L::GB;
-        const unsigned char* vt_p = Vs[buf] + kt * (32 / L::RPI) * L::GB;
-        s[kt] = f32x16{};
-        dp[kt] = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-          s[kt] = Mfma<T>::mma32(*(const u32x4*)(kt_p + r_off[dc]), qf[dc], s[kt]);
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-          dp[kt] = Mfma<T>::mma32(*(const u32x4*)(vt_p + r_off[dc]), gf[dc], dp[kt]);
+  // Tile j: dS and dQ of tile j from (s_cur, p_cur). Pipelined, S^T/dP^T of
+  // tile j+1 go into (s_nxt, p_nxt) meanwhile; otherwise S^T/dP^T of tile j
+  // are computed first, into (s_cur, p_cur).
+  auto tile = [&](int j, f32x16 (&s_cur)[KT], f32x16 (&p_cur)[KT], f32x16 (&s_nxt)[KT],
+                  f32x16 (&p_nxt)[KT], auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    // Every wave is done with tile j-1, so the buffers of the tile loaded
+    // next (j+2 pipelined, j+1 otherwise) are free.
+    __syncthreads();
+    constexpr int AHEAD = PIPE ? 2 : 1;
+    if (FULL || j + AHEAD < ntiles) {
+      load_k(j + AHEAD);
+      load_v(j + AHEAD);
+    }
+    if (FULL || j < w_tiles) {
+      if constexpr (PIPE) {
+        if (FULL || j + 1 < w_tiles) compute_sdp(j + 1, s_nxt, p_nxt);
+      } else {
+        compute_sdp(j, s_cur, p_cur);
       }
-      const bool need_mask = (t0 + BC > kv_end) || (wq0 + 32 > N) || (a.causal && t0 + BC - 1 > wq0);
+      const int t0 = j * BC;
+      const bool need_mask = !FULL && a.causal && t0 + BC - 1 > wq0;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(s[kt][r], sl2, -lse2));
+          float p = fast_exp2(fmaf(s_cur[kt][r], sl2, -lse2));
           if (need_mask) {
             const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool vis = (my_q < N) && key < kv_end && (!a.causal || key <= my_q);
-            p = vis ? p : 0.f;
+            p = (key <= my_q) ? p : 0.f;
           }
-          dp[kt][r] = p * (dp[kt][r] - dsum);
+          p_cur[kt][r] = p * (p_cur[kt][r] - dsum);
         }
       }
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          const u32x4 sf = pack8<T>(dp[kt], 8 * c2);
+          const u32x4 sf = pack8<T>(p_cur[kt], 8 * c2);
           const int rb = (2 * kt + c2) * L::rows16();
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const unsigned char* kp = Ks[buf] + rb + t_off[dt];
+            const unsigned char* kp = Ks[j % NKB] + rb + t_off[dt];
             const u32x2 k0 = lds_read_tr(kp), k1 = lds_read_tr(kp + L::half_step());
             dq[dt] = Mfma<T>::mma32(u32x4{k0.x, k0.y, k1.x, k1.y}, sf, dq[dt]);
           }
@@ -398,6 +451,27 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
+  };
+
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
+  int n_full = a.causal ? (q_blk0 + 1) / BC : ntiles;
+  n_full = min(n_full, ntiles - 1) & ~1;
+  int j = 0;
+  for (; j < n_full; j += 2) {
+    tile(j, s_a, p_a, s_b, p_b, Full{});
+    if constexpr (PIPE) tile(j + 1, s_b, p_b, s_a, p_a, Full{});
+    else tile(j + 1, s_a, p_a, s_b, p_b, Full{});
+  }
+  for (; j < ntiles; ++j) {
+    tile(j, s_a, p_a, s_b, p_b, Part{});
+    if constexpr (PIPE) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        s_a[kt] = s_b[kt];
+        p_a[kt] = p_b[kt];
+      }
+    }
   }
 
   if (my_q < N) {

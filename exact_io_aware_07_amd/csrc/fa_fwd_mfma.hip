@@ -79,10 +79,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
 
   const int N = a.N;
   const int nqb = (N + kBR - 1) / kBR;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nqb;
-  int qb = logical % nqb;
-  if (a.causal) qb = nqb - 1 - qb;  // longest causal blocks first
+  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nqb, a.B * a.H, a.causal);
+  const int bh = pk.bh;
+  const int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;  // causal: last block has most work
   const int b = bh / a.H;
 
   const size_t head_off = (size_t)bh * N * D;

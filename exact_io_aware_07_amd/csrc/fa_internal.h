@@ -198,6 +198,25 @@ __device__ inline void load_tile_lds(__amdgpu_buffer_rsrc_t r, unsigned char* ds
   }
 }
 
+// Block -> (head, block-within-head) for the per-block kernels.
+//  * Non-causal: every block of a head does the same work; blocks of one
+//    head are kept on one XCD (xcd_remap) so its K/V stay in that L2.
+//  * Causal: work differs per block, so blocks are dispatched globally in
+//    decreasing order of work (longest-processing-time first, across all
+//    heads), and the hardware's round-robin over XCDs spreads that order
+//    evenly. `rank` 0 is the block with the most work; the caller maps rank
+//    to its own block index (the last query block, or the first key block).
+struct BlockPick {
+  int bh;
+  int rank;
+};
+__device__ inline int xcd_remap(int bid, int total);
+__device__ inline BlockPick pick_block(int bid, int total, int nblk, int nheads, bool causal) {
+  if (causal) return BlockPick{bid % nheads, bid / nheads};
+  const int logical = xcd_remap(bid, total);
+  return BlockPick{logical / nblk, logical % nblk};
+}
+
 // Block index remap so that consecutive logical blocks run on the same XCD.
 // Workgroups are dealt round-robin to the 8 XCDs; logical block
 // x * per + i is placed on physical slot i * 8 + x. Blocks past the largest
