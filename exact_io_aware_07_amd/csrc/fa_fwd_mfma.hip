@@ -18,7 +18,7 @@
 //  * S^T = K Q^T on v_mfma_f32_32x32x16 (A = 32 keys of the K tile in LDS,
 //    B = the wave's Q rows, resident in VGPRs). In the 32x32 accumulator
 //    lane l holds query l % 32 and 16 keys, so a row's max and sum are
-//    in-lane plus one exchange with lane l ^ 32.
+//    in-lane plus one exchange with lane l ^ 32 (v_permlane32_swap).
 //  * O^T += V^T P^T on the same MFMA. P leaves the S accumulator already in
 //    B-operand order (lane = query, keys in runs of 4). V stays row-major in
 //    LDS; ds_read_b64_tr_b16 hands each lane 4 consecutive keys of one d
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
       }
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = halves_max(mx);
       if (__any(mx > m_ref)) {
         const float m_new = fmaxf(m_ref, mx);
         const float alpha = (m_new == m_ref) ? 1.f : fast_exp2((m_ref - m_new) * sl2);
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
     for (int kt = 0; kt < KT; ++kt) s_a[kt] = s_b[kt];
   }
 
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = halves_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (my_q < N) {
 #pragma unroll

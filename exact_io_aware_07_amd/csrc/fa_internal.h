@@ -113,8 +113,21 @@ struct Mfma<F16> {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value of lane (l ^ 32): the other half of the wave.
-__device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Reductions across the two halves of a wave (lane l with lane l ^ 32) on
+// v_permlane32_swap, a VALU op with no LDS round trip: called with (x, x) it
+// returns, in lanes 0-31, (own, lane + 32) and in lanes 32-63
+// (lane - 32, own), so max / sum of the pair is the two-lane result in
+// every lane.
+__device__ inline float halves_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
 
 // Buffer resource over [base, base + bytes): loads at or past the end read
 // as zero, which is how every kernel here pads ragged tiles.
