@@ -35,6 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # roofline bound of each kernel of the step
 BOUND = {"fwd": "mfma", "dsum": "hbm", "dkdv": "mfma", "dq": "mfma"}
+WARM_SECONDS = 1.5
 
 
 def log(msg: str) -> None:
@@ -102,9 +103,17 @@ def run_gpu(args):
         fa_bwd_dq(q, k, v, do, lse, dsum, dq, w.scale, w.causal, None, stream)
         if ev: ev[4].record(stream)
 
-    log(f"[bench] warmup {args.warmup} steps of {w.name}")
-    for _ in range(args.warmup):
+    # Warm-up: the requested W steps, continued until at least WARM_SECONDS of
+    # GPU work have run, because the clocks take about a second of load to
+    # reach their steady state (a cold first second reads ~15% slow).
+    log(f"[bench] warmup: {args.warmup} steps of {w.name}, at least {WARM_SECONDS} s")
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < args.warmup or time.perf_counter() - t_w < WARM_SECONDS:
         step()
+        n_w += 1
+        if n_w % 50 == 0:
+            torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -186,8 +195,10 @@ def extra_configs(torch, W, iters: int = 10):
         else:
             fn = fwd
             flops = fwd_flops(w)
-        for _ in range(2):
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.3:
             fn()
+            torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for _ in range(iters):

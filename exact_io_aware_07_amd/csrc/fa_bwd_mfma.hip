@@ -196,6 +196,9 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
     const int q0 = it * BQ;
     const bool live = FULL || ((key0 < kv_end) && (!a.causal || q0 + BQ - 1 >= key0));
     if (live) {
+      // Full tiles: let the scheduler interleave the four MFMA chains with
+      // the exponentials and LDS reads (iglp_opt strategy 0).
+      if constexpr (FULL) __builtin_amdgcn_iglp_opt(0);
       const bool need_mask = !FULL && ((key0 + 32 > kv_end) || (a.causal && key0 + 31 > q0));
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
@@ -416,6 +419,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
       load_v(j + AHEAD);
     }
     if (FULL || j < w_tiles) {
+      // Full tiles: raise this wave's issue priority while it runs its MFMA
+      // chains, so the SIMD's other waves fill the gaps around them.
+      if constexpr (FULL) __builtin_amdgcn_s_setprio(1);
       if constexpr (PIPE) {
         if (FULL || j + 1 < w_tiles) compute_sdp(j + 1, s_nxt, p_nxt);
       } else {
@@ -449,6 +455,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
           }
         }
       }
+      if constexpr (FULL) __builtin_amdgcn_s_setprio(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
   };

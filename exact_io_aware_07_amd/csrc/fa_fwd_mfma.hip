@@ -201,7 +201,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
         m_ref = m_new;
       }
 
-      if (FULL || j + 1 < w_tiles) compute_s((j + 1) & 1, s_nxt);
+      // Main block of a full tile: ask the scheduler to interleave the MFMA
+    // chains with the exponentials and LDS reads (iglp_opt strategy 0) and
+    // raise this wave's issue priority while it runs, so the SIMD's other
+    // waves fill the gaps rather than the other way round.
+    if constexpr (FULL) {
+      __builtin_amdgcn_iglp_opt(0);
+      __builtin_amdgcn_s_setprio(1);
+    }
+    if (FULL || j + 1 < w_tiles) compute_s((j + 1) & 1, s_nxt);
 
       const float mref2 = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
       float lsum = 0.f;
@@ -237,6 +245,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
           }
         }
       }
+      if constexpr (FULL) __builtin_amdgcn_s_setprio(0);
     }
     // This wave's loads for the next tiles must have landed before anyone
     // passes the next barrier.
