@@ -2,8 +2,8 @@
 """Throughput of exact attention (forward + backward) on one MI355X.
 
 One step is the whole hot path on one batch of seeded synthetic input:
-fa_fwd, then the backward as the three launches fa_bwd enqueues
-(fa_bwd_dsum, fa_bwd_dkdv, fa_bwd_dq), all on one stream. The workload is the
+fa_fwd, then the backward as the two launches fa_bwd enqueues (fa_bwd_dq,
+which also forms D_i = rowsum(dO * O), then fa_bwd_dkdv), all on one stream. The workload is the
 GPT-2-shaped forward+backward case: B=8, H=12, N=1024, d=64, bf16, causal,
 Q, K, V, dO ~ N(0, 1) from seed 0 (the only listed workload with a
 backward; the other shapes are parity-test cases and appear here only under
@@ -34,7 +34,7 @@ PEAK_HBM_BYTES = 8.0e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # roofline bound of each kernel of the step
-BOUND = {"fwd": "mfma", "dsum": "hbm", "dkdv": "mfma", "dq": "mfma"}
+BOUND = {"fwd": "mfma", "dq": "mfma", "dkdv": "mfma"}
 WARM_SECONDS = 1.5
 
 
@@ -56,8 +56,6 @@ def kernel_work(name: str, w) -> float:
         return 8.0 * w.d * pairs                   # S recompute, dP, dV, dK
     if name == "dq":
         return 2.0 * w.d * pairs                   # dQ (its S/dP recompute is overhead)
-    if name == "dsum":
-        return w.B * w.H * w.N * (2.0 * w.d * w.elem_bytes + 4.0)  # read O, dO; write D
     raise KeyError(name)
 
 
@@ -77,7 +75,7 @@ def traffic_for(name: str, workload: str):
 
 def run_gpu(args):
     import torch
-    from exact_io_aware_07_amd import (fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dsum, fa_fwd, lib)
+    from exact_io_aware_07_amd import fa_bwd_dkdv, fa_bwd_dq, fa_fwd, lib
     from exact_io_aware_07_amd import workloads as W
 
     if not torch.cuda.is_available():
@@ -96,12 +94,10 @@ def run_gpu(args):
         if ev: ev[0].record(stream)
         fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, stream)
         if ev: ev[1].record(stream)
-        fa_bwd_dsum(o, do, dsum, stream)
+        fa_bwd_dq(q, k, v, o, do, lse, dsum, dq, w.scale, w.causal, None, stream)
         if ev: ev[2].record(stream)
         fa_bwd_dkdv(q, k, v, do, lse, dsum, dk, dv, w.scale, w.causal, None, stream)
         if ev: ev[3].record(stream)
-        fa_bwd_dq(q, k, v, do, lse, dsum, dq, w.scale, w.causal, None, stream)
-        if ev: ev[4].record(stream)
 
     # Warm-up: the requested W steps, continued until at least WARM_SECONDS of
     # GPU work have run, because the clocks take about a second of load to
@@ -114,7 +110,7 @@ def run_gpu(args):
         n_w += 1
         if n_w % 50 == 0:
             torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -122,7 +118,7 @@ def run_gpu(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    names = ["fwd", "dsum", "dkdv", "dq"]
+    names = ["fwd", "dq", "dkdv"]
     avg_ms = {n: statistics.fmean(ev[j].elapsed_time(ev[j + 1]) for ev in events)
               for j, n in enumerate(names)}
     log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step; kernels (ms) {avg_ms}")
@@ -171,7 +167,7 @@ def run_gpu(args):
                    "flop_convention": "fwd 4BHN^2d, bwd 2.5x fwd, x0.5 causal"},
         "pct_of_bf16_peak": 100.0 * value * 1e12 / PEAK_BF16_FLOPS,
         "fwd_tflops": f_fwd / (avg_ms["fwd"] * 1e-3) / 1e12,
-        "bwd_tflops": f_bwd / ((avg_ms["dsum"] + avg_ms["dkdv"] + avg_ms["dq"]) * 1e-3) / 1e12,
+        "bwd_tflops": f_bwd / ((avg_ms["dq"] + avg_ms["dkdv"]) * 1e-3) / 1e12,
         "kernels": kernels,
         "roofline": roof,
     }

@@ -95,7 +95,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
       workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
   return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d,
-                    scale, causal, stream, dtype, (int)fa::BwdStage::ALL);
+                    scale, causal, stream, dtype,
+                    (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV);
 }
 
 int fa_bwd_dsum(const void* o, const void* dout, float* dsum, int B, int H, int N, int d,
@@ -126,20 +127,20 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
                     d, scale, causal, stream, dtype, (int)fa::BwdStage::DKDV);
 }
 
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-              const float* dsum, void* dq, int B, int H, int N, int d, float scale, int causal,
-              const int* kv_len, void* stream, int dtype) {
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, float* dsum, void* dq, int B, int H, int N, int d, float scale,
+              int causal, const int* kv_len, void* stream, int dtype) {
   int st = check_scalars(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H * N == 0) return FA_OK;
-  if (!q || !k || !v || !dout || !lse || !dsum || !dq) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned4(lse) || !aligned4(dsum))
+  if (!q || !k || !v || !o || !dout || !lse || !dsum || !dq) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned4(lse) || !aligned4(dsum))
     return FA_ERR_INVALID_ARG;
   if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
-  return launch_bwd(q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, (float*)dsum, kv_len, B, H,
-                    N, d, scale, causal, stream, dtype, (int)fa::BwdStage::DQ);
+  return launch_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, dsum, kv_len, B, H, N, d, scale,
+                    causal, stream, dtype, (int)fa::BwdStage::DQ);
 }
 
 const char* fa_strerror(int status) {

@@ -11,21 +11,25 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
 //   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three launches, no atomics, so the result is bit-reproducible:
-//   1. dsum_kernel:  D_i = rowsum(dO * O) into the caller's workspace.
-//   2. dkdv_kernel:  one workgroup per key block; K and V stay in VGPRs, the
+// Two launches, no atomics, so the result is bit-reproducible (a third,
+// dsum_kernel, computes D_i = rowsum(dO * O) on its own for callers who want
+// that stage alone):
+//   2. dkdv_kernel:  one workgroup per key block, after dq_kernel (it reads
+//      D from the workspace); K and V stay in VGPRs, the
 //      loop streams query tiles (Q, dO from HBM straight into LDS; LSE, D)
 //      past them. Per tile: S = Q K^T and dP = dO V^T with the key as the
 //      accumulator column (lane), so P and dS come out of the accumulator
 //      already in the layout the next two products take as B operand:
 //      dV^T += dO^T P, dK^T += Q^T dS, whose A operands (dO^T, Q^T) are
 //      transposed reads (ds_read_b64_tr_b16) of the same row-major tiles.
-//   3. dq_kernel: one workgroup per query block; Q and dO stay in VGPRs, the
+//   1. dq_kernel: one workgroup per query block; it first forms D_i =
+//      rowsum(dO * O) for its rows and writes it to the workspace; Q and dO
+//      stay in VGPRs, the
 //      loop streams key tiles (K, V) through LDS. Per tile: S^T = K Q^T and
 //      dP^T = V dO^T with the query as the lane, then dQ^T += K^T dS^T with
 //      K^T a transposed read of the K tile.
-// Kernel 3 recomputes S and dP, so the MFMA work is 7 products per tile pair
-// against the 5 the gradients need.
+// The dQ kernel recomputes S and dP, so the MFMA work is 7 products per tile
+// pair against the 5 the gradients need.
 #include <type_traits>
 
 #include "fa_internal.h"
@@ -354,11 +358,27 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
     qf[dc] = buf_load16(rq, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
     gf[dc] = buf_load16(rg, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
   }
-  float lse2 = 0.f, dsum = 0.f;
+  // D_i = sum_c dO_ic O_ic for this lane's row, from the dO fragments
+  // already in VGPRs and the matching O fragments (this half of the wave
+  // holds half of the row; the halves are summed). Written to the workspace
+  // for the dK/dV kernel, which runs after this one.
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const uint16_t*)a.o + head_off, (uint32_t)N * D * 2);
+  float dsum = 0.f;
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) {
+    const u32x4 of = buf_load16(ro, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dsum = fmaf(Mfma<T>::to_f32(of[i] & 0xffffu), Mfma<T>::to_f32(gf[dc][i] & 0xffffu), dsum);
+      dsum = fmaf(Mfma<T>::to_f32(of[i] >> 16), Mfma<T>::to_f32(gf[dc][i] >> 16), dsum);
+    }
+  }
+  dsum = halves_sum(dsum);
+  float lse2 = 0.f;
   if (my_q < N) {
     const float l = a.lse[(size_t)bh * N + my_q];
     lse2 = (l == -INFINITY) ? 0.f : l * kLog2e;
-    dsum = a.dsum[(size_t)bh * N + my_q];
+    if (hh == 0) a.dsum[(size_t)bh * N + my_q] = dsum;
   }
   const float sl2 = a.scale * kLog2e;
 
@@ -506,15 +526,15 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
                        st, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dsum, rows);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (stages & (int)BwdStage::DKDV) {
-    const long nkb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nkb)),
-                       dim3(kBwdThreads), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   if (stages & (int)BwdStage::DQ) {
     const long nqb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
     hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nqb)),
+                       dim3(kBwdThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (stages & (int)BwdStage::DKDV) {
+    const long nkb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nkb)),
                        dim3(kBwdThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

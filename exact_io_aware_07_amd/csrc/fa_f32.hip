@@ -266,11 +266,20 @@ __global__ __launch_bounds__(kT) void dq_f32_kernel(BwdArgs a) {
     g[e] = (my_q < N) ? Gg[(size_t)my_q * D + part * 32 + e] : 0.f;
     dq[e] = 0.f;
   }
-  float lse2 = 0.f, dsum = 0.f;
+  // D_i = sum_c dO_ic O_ic for this row (G lanes share it), written to the
+  // workspace for the dK/dV kernel, which runs after this one.
+  float dsum = 0.f;
+  if (my_q < N) {
+    const float* Og = (const float*)a.o + head_off + (size_t)my_q * D + part * 32;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) dsum = fmaf(Og[e], g[e], dsum);
+  }
+  dsum = group_sum<G>(dsum);
+  float lse2 = 0.f;
   if (my_q < N) {
     const float l = a.lse[(size_t)bh * N + my_q];
     lse2 = (l == -INFINITY) ? 0.f : l * kLog2e;
-    dsum = a.dsum[(size_t)bh * N + my_q];
+    if (part == 0) a.dsum[(size_t)bh * N + my_q] = dsum;
   }
   const float sl2 = a.scale * kLog2e;
 
@@ -329,12 +338,12 @@ hipError_t bwd_launch(const BwdArgs& a, int stages, hipStream_t s) {
   }
   constexpr int PB = kT / (D / 32);
   const long nb = (a.N + PB - 1) / PB;
-  if (stages & (int)BwdStage::DKDV) {
-    hipLaunchKernelGGL(dkdv_f32_kernel<D>, dim3((unsigned)((long)a.B * a.H * nb)), dim3(kT), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   if (stages & (int)BwdStage::DQ) {
     hipLaunchKernelGGL(dq_f32_kernel<D>, dim3((unsigned)((long)a.B * a.H * nb)), dim3(kT), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (stages & (int)BwdStage::DKDV) {
+    hipLaunchKernelGGL(dkdv_f32_kernel<D>, dim3((unsigned)((long)a.B * a.H * nb)), dim3(kT), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return e;

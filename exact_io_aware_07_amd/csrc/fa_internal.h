@@ -42,8 +42,9 @@ struct BwdArgs {
 // by the caller.
 hipError_t launch_fwd_mfma(const FwdArgs& a, Elem in, Elem out, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
-// Backward stages: D_i = rowsum(dO * O), then dK/dV, then dQ. The dK/dV and
-// dQ stages read only the inputs, LSE and D, so they may run in any order.
+// Backward stages, launched in this order when several are asked for: the
+// stand-alone D_i = rowsum(dO * O), then dQ (which also forms D_i for its
+// rows and writes it to the workspace), then dK/dV (which reads D_i).
 enum class BwdStage { DSUM = 1, DKDV = 2, DQ = 4, ALL = 7 };
 hipError_t launch_bwd_mfma(const BwdArgs& a, Elem t, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);

@@ -50,7 +50,7 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_dsum.restype = i
     L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
     L.fa_bwd_dkdv.restype = i
-    L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
+    L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
     L.fa_bwd_dq.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
@@ -141,7 +141,7 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False
 
 
 def fa_bwd_dsum(o, dout, dsum, stream=None) -> None:
-    """Stage 1 of the backward: dsum[b, h, i] = sum_c dout * o (fp32 [B, H, N])."""
+    """D_i alone: dsum[b, h, i] = sum_c dout * o (fp32 [B, H, N])."""
     B, H, N, d = o.shape
     _check_tensor("o", o, o.shape)
     _check_tensor("dout", dout, o.shape, o.dtype)
@@ -154,7 +154,7 @@ def fa_bwd_dsum(o, dout, dsum, stream=None) -> None:
 
 def fa_bwd_dkdv(q, k, v, dout, lse, dsum, dk, dv, scale: float, causal: bool = False,
                 kv_len: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Stage 2 of the backward: writes dk, dv."""
+    """Backward stage after fa_bwd_dq (or fa_bwd_dsum): writes dk, dv."""
     B, H, N, d = q.shape
     for name, t in (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype)
@@ -168,17 +168,17 @@ def fa_bwd_dkdv(q, k, v, dout, lse, dsum, dk, dv, scale: float, causal: bool = F
         raise FaError(st, "fa_bwd_dkdv")
 
 
-def fa_bwd_dq(q, k, v, dout, lse, dsum, dq, scale: float, causal: bool = False,
+def fa_bwd_dq(q, k, v, o, dout, lse, dsum, dq, scale: float, causal: bool = False,
               kv_len: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Stage 3 of the backward: writes dq."""
+    """Backward stage: writes dq and dsum (D_i = rowsum(dout * o), fp32 [B, H, N])."""
     B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq)):
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)):
         _check_tensor(name, t, q.shape, q.dtype)
     _check_tensor("q", q, q.shape)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     _check_tensor("dsum", dsum, (B, H, N), torch.float32)
-    st = lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dsum), _ptr(dq),
-                         B, H, N, d, float(scale), int(bool(causal)), _kv(kv_len, B),
+    st = lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dsum),
+                         _ptr(dq), B, H, N, d, float(scale), int(bool(causal)), _kv(kv_len, B),
                          _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_dq")

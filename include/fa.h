@@ -100,16 +100,16 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            void* stream, int dtype);
 
 /*
- * The backward as its three stages, for callers that want to time them or
- * overlap the last two on separate streams. fa_bwd enqueues exactly
- * fa_bwd_dsum, then fa_bwd_dkdv, then fa_bwd_dq on one stream. Arguments
+ * The backward as its stages, for callers that want to time them. fa_bwd
+ * enqueues exactly fa_bwd_dq, then fa_bwd_dkdv, on one stream. Arguments
  * mean what they mean for fa_bwd; dsum is the fp32 [B,H,N] array
- * D_i = sum_c dO_ic * O_ic (the workspace of fa_bwd), written by
- * fa_bwd_dsum and read by the other two, which depend on nothing else that
- * the other writes and may therefore run in either order or concurrently.
- *   fa_bwd_dsum: reads o, dout; writes dsum (4-byte aligned).
- *   fa_bwd_dkdv: reads q, k, v, dout, lse, dsum; writes dk, dv.
- *   fa_bwd_dq:   reads q, k, v, dout, lse, dsum; writes dq.
+ * D_i = sum_c dO_ic * O_ic (the workspace of fa_bwd).
+ *   fa_bwd_dq:   reads q, k, v, o, dout, lse; writes dq and dsum (it forms
+ *                D_i for its own rows; dsum 4-byte aligned).
+ *   fa_bwd_dkdv: reads q, k, v, dout, lse, dsum; writes dk, dv. dsum must
+ *                hold D_i, from fa_bwd_dq or fa_bwd_dsum, before it runs.
+ *   fa_bwd_dsum: reads o, dout; writes dsum. The same D_i on its own, for a
+ *                caller that wants dK/dV without dQ.
  * Errors as for fa_bwd (no FA_ERR_WORKSPACE: dsum is a plain argument).
  */
 int fa_bwd_dsum(const void* o, const void* dout, float* dsum, int B, int H,
@@ -118,10 +118,10 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                 const float* lse, const float* dsum, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal,
                 const int* kv_len, void* stream, int dtype);
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-              const float* lse, const float* dsum, void* dq, int B, int H,
-              int N, int d, float scale, int causal, const int* kv_len,
-              void* stream, int dtype);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, float* dsum, void* dq,
+              int B, int H, int N, int d, float scale, int causal,
+              const int* kv_len, void* stream, int dtype);
 
 /* Static, human-readable text for a status code. Never NULL. */
 const char* fa_strerror(int status);

@@ -136,9 +136,13 @@ def test_stage_entry_points_validate_before_launch():
                          fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
     assert L.fa_bwd_dkdv(A, A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 3, None, None,
                          fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_bwd_dq(A, A, A, A, A, A, None, 1, 1, 16, 64, 0.125, 0, None, None,
+    assert L.fa_bwd_dq(A, A, A, A, A, A, A, None, 1, 1, 16, 64, 0.125, 0, None, None,
                        fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_bwd_dq(A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None, 9) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_bwd_dq(A, A, A, None, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None,
+                       fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dq(A, A, A, A, A, A, A + 2, A, 1, 1, 16, 64, 0.125, 0, None, None,
+                       fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dq(A, A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None, 9) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_sequence_longer_than_a_32_bit_head_is_unsupported():
