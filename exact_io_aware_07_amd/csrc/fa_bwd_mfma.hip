@@ -287,37 +287,31 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 // dQ: one workgroup per (b, h, query block of 128 rows); wave w owns rows
 // [32w, 32w + 32) with its Q and dO rows in VGPRs. Key tiles of BC keys (K,
 // V straight from HBM into LDS) stream past; K is read both row-wise (A of
-// S^T) and transposed (A of dQ^T). At d = 64 the tiles are software
-// pipelined: S^T and dP^T of tile j+1 are computed in the same basic block
-// as dS and dQ of tile j, so K runs through three LDS buffers (tile j for
-// dQ, j+1 for S, j+2 loading) and V through two.
+// S^T) and transposed (A of dQ^T). Tiles of 64 keys, double-buffered; the
+// next tile's loads are in flight while the current one is computed.
+// (Computing S/dP of the next tile alongside the current one was measured
+// slower than three waves per SIMD without it, at d = 64.)
 //
 // Rows past N and keys past kv_len need no mask here: their Q/dO or K/V
 // rows read as zero, so their dS (or their K row) is zero and they add
 // nothing to dQ. Only the causal diagonal is masked.
 template <int D>
 struct DqCfg {
-  // d = 64: pipelined, 32-key tiles. d = 128: the pipeline's second set of
-  // S/dP registers would cost the second wave per SIMD, which is worth
-  // more, so tiles of 64 keys are computed one at a time.
-  static constexpr bool PIPE = (D == 64);
-  static constexpr int BC = PIPE ? 32 : 64;  // keys per tile
-  static constexpr int NKB = PIPE ? 3 : 2;   // K tile buffers
+  static constexpr int BC = 64;                    // keys per tile
+  static constexpr int MINW = (D == 64) ? 3 : 2;  // waves per SIMD the registers allow
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs a) {
   using L = TileLayout<D>;
   constexpr int BR = 32 * kBwdWaves;
-  constexpr bool PIPE = DqCfg<D>::PIPE;
   constexpr int BC = DqCfg<D>::BC;
-  constexpr int NKB = DqCfg<D>::NKB;
   constexpr int KT = BC / 32;
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
   constexpr int TB = L::bytes(BC);
 
-  __shared__ __attribute__((aligned(1024))) unsigned char Ks[NKB][TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TB];
   __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TB];
 
   const int tid = threadIdx.x;
@@ -393,12 +387,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  auto load_k = [&](int j) { load_tile_lds<D, BC, kBwdWaves>(rk, Ks[j % NKB], j * BC, wave, lane); };
+  auto load_k = [&](int j) { load_tile_lds<D, BC, kBwdWaves>(rk, Ks[j & 1], j * BC, wave, lane); };
   auto load_v = [&](int j) { load_tile_lds<D, BC, kBwdWaves>(rv, Vs[j & 1], j * BC, wave, lane); };
   auto compute_sdp = [&](int j, f32x16 (&s)[KT], f32x16 (&dp)[KT]) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      const unsigned char* kp = Ks[j % NKB] + kt * (32 / L::RPI) * L::GB;
+      const unsigned char* kp = Ks[j & 1] + kt * (32 / L::RPI) * L::GB;
       const unsigned char* vp = Vs[j & 1] + kt * (32 / L::RPI) * L::GB;
       s[kt] = f32x16{};
       dp[kt] = f32x16{};
@@ -409,44 +403,28 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
     }
   };
 
-  f32x16 s_a[KT], s_b[KT], p_a[KT], p_b[KT];
   if (ntiles > 0) {
     load_k(0);
     load_v(0);
-    if (PIPE && ntiles > 1) {
-      load_k(1);
-      load_v(1);
-    }
     __builtin_amdgcn_s_waitcnt(0);
-    if constexpr (PIPE) {
-      __syncthreads();
-      if (w_tiles > 0) compute_sdp(0, s_a, p_a);
-    }
   }
 
-  // Tile j: dS and dQ of tile j from (s_cur, p_cur). Pipelined, S^T/dP^T of
-  // tile j+1 go into (s_nxt, p_nxt) meanwhile; otherwise S^T/dP^T of tile j
-  // are computed first, into (s_cur, p_cur).
-  auto tile = [&](int j, f32x16 (&s_cur)[KT], f32x16 (&p_cur)[KT], f32x16 (&s_nxt)[KT],
-                  f32x16 (&p_nxt)[KT], auto full) {
+  // Tile j: S^T/dP^T, then dS and dQ. Full tiles (no causal mask for any
+  // row of the workgroup) run with no liveness test.
+  auto tile = [&](int j, auto full) {
     constexpr bool FULL = decltype(full)::value;
-    // Every wave is done with tile j-1, so the buffers of the tile loaded
-    // next (j+2 pipelined, j+1 otherwise) are free.
+    // Every wave is done with tile j-1, so its buffers take tile j+1.
     __syncthreads();
-    constexpr int AHEAD = PIPE ? 2 : 1;
-    if (FULL || j + AHEAD < ntiles) {
-      load_k(j + AHEAD);
-      load_v(j + AHEAD);
+    if (FULL || j + 1 < ntiles) {
+      load_k(j + 1);
+      load_v(j + 1);
     }
     if (FULL || j < w_tiles) {
       // Full tiles: raise this wave's issue priority while it runs its MFMA
       // chains, so the SIMD's other waves fill the gaps around them.
       if constexpr (FULL) __builtin_amdgcn_s_setprio(1);
-      if constexpr (PIPE) {
-        if (FULL || j + 1 < w_tiles) compute_sdp(j + 1, s_nxt, p_nxt);
-      } else {
-        compute_sdp(j, s_cur, p_cur);
-      }
+      f32x16 s_cur[KT], p_cur[KT];
+      compute_sdp(j, s_cur, p_cur);
       const int t0 = j * BC;
       const bool need_mask = !FULL && a.causal && t0 + BC - 1 > wq0;
 #pragma unroll
@@ -469,7 +447,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
           const int rb = (2 * kt + c2) * L::rows16();
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const unsigned char* kp = Ks[j % NKB] + rb + t_off[dt];
+            const unsigned char* kp = Ks[j & 1] + rb + t_off[dt];
             const u32x2 k0 = lds_read_tr(kp), k1 = lds_read_tr(kp + L::half_step());
             dq[dt] = Mfma<T>::mma32(u32x4{k0.x, k0.y, k1.x, k1.y}, sf, dq[dt]);
           }
@@ -482,24 +460,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdArgs a) {
 
   using Full = std::integral_constant<bool, true>;
   using Part = std::integral_constant<bool, false>;
+  // Tiles that no row of the workgroup sees only partly (causal) form the
+  // main loop; a full tile also loads the next one unconditionally, so it
+  // must not be the last.
   int n_full = a.causal ? (q_blk0 + 1) / BC : ntiles;
-  n_full = min(n_full, ntiles - 1) & ~1;
+  n_full = min(n_full, ntiles - 1);
   int j = 0;
-  for (; j < n_full; j += 2) {
-    tile(j, s_a, p_a, s_b, p_b, Full{});
-    if constexpr (PIPE) tile(j + 1, s_b, p_b, s_a, p_a, Full{});
-    else tile(j + 1, s_a, p_a, s_b, p_b, Full{});
+  for (; j + 1 < n_full; j += 2) {
+    tile(j, Full{});
+    tile(j + 1, Full{});
   }
-  for (; j < ntiles; ++j) {
-    tile(j, s_a, p_a, s_b, p_b, Part{});
-    if constexpr (PIPE) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        s_a[kt] = s_b[kt];
-        p_a[kt] = p_b[kt];
-      }
-    }
-  }
+  for (; j < n_full; ++j) tile(j, Full{});
+  for (; j < ntiles; ++j) tile(j, Part{});
 
   if (my_q < N) {
     uint16_t* dQg = (uint16_t*)a.dq + head_off + (size_t)my_q * D;
