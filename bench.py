@@ -13,6 +13,10 @@ Algorithmic work (what the method must do, not what the kernels happen to
 do): forward 4*B*H*N^2*d, backward 2.5x that (five N^2 d products: S
 recompute, dP, dV, dK, dQ), both halved for causal.
 
+The timed region is K whole steps with nothing else on the stream. Each
+kernel's average duration (for the roofline object) is then taken with two
+HIP events around K back-to-back launches of that kernel alone.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -90,14 +94,17 @@ def run_gpu(args):
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev: ev[0].record(stream)
-        fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, stream)
-        if ev: ev[1].record(stream)
-        fa_bwd_dq(q, k, v, o, do, lse, dsum, dq, w.scale, w.causal, None, stream)
-        if ev: ev[2].record(stream)
-        fa_bwd_dkdv(q, k, v, do, lse, dsum, dk, dv, w.scale, w.causal, None, stream)
-        if ev: ev[3].record(stream)
+    kernels_fn = {
+        "fwd": lambda: fa_fwd(q, k, v, o, lse, w.scale, w.causal, None, stream),
+        "dq": lambda: fa_bwd_dq(q, k, v, o, do, lse, dsum, dq, w.scale, w.causal, None, stream),
+        "dkdv": lambda: fa_bwd_dkdv(q, k, v, do, lse, dsum, dk, dv, w.scale, w.causal, None,
+                                    stream),
+    }
+    names = ["fwd", "dq", "dkdv"]
+
+    def step():
+        for n in names:
+            kernels_fn[n]()
 
     # Warm-up: the requested W steps, continued until at least WARM_SECONDS of
     # GPU work have run, because the clocks take about a second of load to
@@ -110,17 +117,26 @@ def run_gpu(args):
         n_w += 1
         if n_w % 50 == 0:
             torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: K whole steps, nothing else on the stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    names = ["fwd", "dq", "dkdv"]
-    avg_ms = {n: statistics.fmean(ev[j].elapsed_time(ev[j + 1]) for ev in events)
-              for j, n in enumerate(names)}
+    # Per-kernel duration: two HIP events on the launch stream around K
+    # back-to-back launches of that kernel alone (an event between two
+    # kernels of a step would add its own few microseconds to each).
+    avg_ms = {}
+    for n in names:
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            kernels_fn[n]()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        avg_ms[n] = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step; kernels (ms) {avg_ms}")
 
     f_fwd = fwd_flops(w)
@@ -169,6 +185,7 @@ def run_gpu(args):
         "fwd_tflops": f_fwd / (avg_ms["fwd"] * 1e-3) / 1e12,
         "bwd_tflops": f_bwd / ((avg_ms["dq"] + avg_ms["dkdv"]) * 1e-3) / 1e12,
         "kernels": kernels,
+        "kernel_sum_us": sum(avg_ms.values()) * 1e3,
         "roofline": roof,
     }
     if not args.no_extra:

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 
   const int N = a.N;
   const int nkb = (N + BK - 1) / BK;
-  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nkb, a.B * a.H, a.causal);
+  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nkb, a.B * a.H, a.causal, DkdvCfg<D>::MINW);
   const int bh = pk.bh;
   const int kb = pk.rank;  // causal: key block 0 sees every query and has the most work
   const int b = bh / a.H;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
 
   const int N = a.N;
   const int nqb = (N + BR - 1) / BR;
-  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nqb, a.B * a.H, a.causal);
+  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nqb, a.B * a.H, a.causal, DqCfg<D>::MINW);
   const int bh = pk.bh;
   const int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;
   const int b = bh / a.H;

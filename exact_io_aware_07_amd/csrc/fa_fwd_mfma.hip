@@ -56,11 +56,12 @@ constexpr int kBR = 32 * kWaves;  // query rows per workgroup
 
 template <int D>
 struct FwdTile {
-  static constexpr int BC = 64;  // keys per tile
+  static constexpr int BC = 64;                    // keys per tile
+  static constexpr int OCC = (D == 64) ? 3 : 2;  // waves per SIMD the registers allow
 };
 
 template <typename T, int D, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(FwdArgs a) {
   using L = TileLayout<D>;
   constexpr int BC = FwdTile<D>::BC;
   constexpr int KT = BC / 32;                   // 32-key sub-tiles
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_mfma_kernel(Fwd
 
   const int N = a.N;
   const int nqb = (N + kBR - 1) / kBR;
-  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nqb, a.B * a.H, a.causal);
+  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nqb, a.B * a.H, a.causal, FwdTile<D>::OCC);
   const int bh = pk.bh;
   const int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;  // causal: last block has most work
   const int b = bh / a.H;

@@ -156,17 +156,25 @@ __device__ inline u32x2 lds_read_tr(const void* p) {
 // LDS layout of a [rows][D] 16-bit tile filled by direct loads: groups of
 // RPI rows (1 KiB, one buffer_load ... lds per wave), each group padded by
 // 16 bytes; inside a group, logical 16-byte chunk c of row r' sits at
-// position c ^ sw(r'). For D = 128 (4 rows per group) sw = 4 r'; for D = 64
-// (8 rows) sw = 2 (r' / 2). With the pad, 16 lanes reading one chunk of 16
-// consecutive rows, and 16 lanes reading two adjacent chunks of 4
-// consecutive rows (the transposed-read pattern), fall on distinct banks.
+// position c ^ sw(r'). LDS has 64 banks of 4 bytes: a 16-byte read is served
+// 16 lanes per cycle, an 8-byte transposed read 32 lanes per cycle. Both
+// patterns must fall on distinct banks: 16 lanes reading one chunk of 16
+// consecutive rows, and 32 lanes reading four adjacent chunks (an aligned
+// half-row of 4 chunks) of 4 consecutive rows. For D = 128 (4 rows per
+// group, one row per 256-byte bank window) sw = 4 r'. For D = 64 (8 rows,
+// two per bank window) sw is 2 x the bit-reversed r' / 2, i.e. 0 0 4 4 2 2
+// 6 6: rows r' and r' + 2 then use opposite 4-chunk halves, and the four
+// rows of one parity use four distinct even offsets, which the 16-byte group
+// pad turns odd for the next group.
 template <int D>
 struct TileLayout {
   static constexpr int RB = D * 2;       // bytes per row
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int RPI = 1024 / RB;  // rows per 1 KiB group
   static constexpr int GB = 1024 + 16;   // bytes per group incl. pad
-  __device__ static constexpr int sw(int r) { return D == 128 ? 4 * r : 2 * (r >> 1); }
+  __device__ static constexpr int sw(int r) {
+    return D == 128 ? 4 * r : ((((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1));
+  }
   // byte offset of logical (row, chunk) inside a tile
   __device__ static constexpr int off(int row, int chunk) {
     return (row / RPI) * GB + (row % RPI) * RB + ((chunk ^ sw(row % RPI)) << 4);
@@ -215,18 +223,64 @@ __device__ inline void load_tile_lds(__amdgpu_buffer_rsrc_t r, unsigned char* ds
 // Block -> (head, block-within-head) for the per-block kernels.
 //  * Non-causal: every block of a head does the same work; blocks of one
 //    head are kept on one XCD (xcd_remap) so its K/V stay in that L2.
-//  * Causal: work differs per block, so blocks are dispatched globally in
-//    decreasing order of work (longest-processing-time first, across all
-//    heads), and the hardware's round-robin over XCDs spreads that order
-//    evenly. `rank` 0 is the block with the most work; the caller maps rank
-//    to its own block index (the last query block, or the first key block).
+//  * Causal: work differs per block. Item i = (head i % nheads, rank
+//    i / nheads) has work proportional to nblk - rank, so items in index
+//    order are in decreasing order of work; `rank` 0 is the block with the
+//    most work and the caller maps it to its own block index (the last
+//    query block, or the first key block). causal_item() chooses which item
+//    each workgroup runs (see there).
 struct BlockPick {
   int bh;
   int rank;
 };
+
+// Causal dispatch on MI355X. Workgroup bid runs on XCD bid % 8; the u-th
+// workgroup of an XCD (u = bid / 8) goes to CU position u % 32 of that XCD
+// while the kernel's first `occ` workgroups per CU are being placed (all of
+// them resident at once), and later ones go wherever a slot frees. Items
+// stay on the XCD of their index (item 8j + x on XCD x, so a head keeps its
+// K/V in one L2 when nheads is a multiple of 8), and within an XCD the
+// resident set is filled greedily, longest first: round 0 (u < 32) takes the
+// 32 longest items in order, round 1 takes the next 32 in reverse, so the
+// CU with the shortest first item gets the longest second one, and round 2
+// (occ >= 3) gives its longest item to the CU that rounds 0 and 1 left least
+// loaded. Workgroups from round 3 on, and past the resident set, keep
+// longest-first order. Any order is correct; this one evens out the work
+// per CU when the whole grid fits on the chip at once (fewer than about
+// three blocks per CU), where plain longest-first order leaves the CUs that
+// drew three long blocks running alone at the end.
+constexpr int kCusPerXcd = 32;
+__device__ inline int causal_item(int bid, int total, int nblk, int nheads, int occ) {
+  const int x = bid & 7;
+  const int u = bid >> 3;
+  if (u < kCusPerXcd || u >= kCusPerXcd * min(occ, 3)) return bid;
+  const int n = (total - x + 7) >> 3;  // workgroups (and items) of this XCD
+  const int rho = u / kCusPerXcd;
+  const int c = u % kCusPerXcd;
+  const int m = min(n - rho * kCusPerXcd, kCusPerXcd);  // positions used by this round
+  if (rho == 1) return 8 * (kCusPerXcd + (m - 1 - c)) + x;
+  // Round 2: load of position p after rounds 0 and 1 is w(p) + w(63 - p)
+  // (round 1 is full, since round 2 exists); rank this position among the
+  // round's m positions by that load (ties: lower position first). One lane
+  // per position, then a ballot.
+  auto w = [&](int j) { return nblk - (8 * j + x) / nheads; };
+  const int p = threadIdx.x & (kCusPerXcd - 1);
+  const int lane = threadIdx.x & 63;
+  const int l_me = w(c) + w(2 * kCusPerXcd - 1 - c);
+  const int l_p = w(p) + w(2 * kCusPerXcd - 1 - p);
+  const bool before = lane < kCusPerXcd && p < m && (l_p < l_me || (l_p == l_me && p < c));
+  const int r = __popcll(__ballot(before));
+  return 8 * (2 * kCusPerXcd + r) + x;
+}
+
 __device__ inline int xcd_remap(int bid, int total);
-__device__ inline BlockPick pick_block(int bid, int total, int nblk, int nheads, bool causal) {
-  if (causal) return BlockPick{bid % nheads, bid / nheads};
+// occ: workgroups of this kernel that fit on one CU at once.
+__device__ inline BlockPick pick_block(int bid, int total, int nblk, int nheads, bool causal,
+                                       int occ) {
+  if (causal) {
+    const int i = causal_item(bid, total, nblk, nheads, occ);
+    return BlockPick{i % nheads, i / nheads};
+  }
   const int logical = xcd_remap(bid, total);
   return BlockPick{logical / nblk, logical % nblk};
 }
