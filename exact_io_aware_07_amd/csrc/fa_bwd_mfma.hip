@@ -92,10 +92,21 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   constexpr int DT = D / 32;
   constexpr int TB = L::bytes(BQ);
 
-  __shared__ __attribute__((aligned(1024))) unsigned char Qs[2][TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char Gs[2][TB];  // dO
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];            // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];            // D_i
+  // Double buffers of Q, dO, LSE (times log2 e) and D as separate variables,
+  // so the compiler can tell a copy into one buffer from reads of the other.
+  // Query tile it uses the buffers of parity it & 1.
+  __shared__ __attribute__((aligned(1024))) unsigned char Qs0[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Qs1[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Gs0[TB];  // dO
+  __shared__ __attribute__((aligned(1024))) unsigned char Gs1[TB];
+  __shared__ __attribute__((aligned(16))) float Ls0[BQ];
+  __shared__ __attribute__((aligned(16))) float Ls1[BQ];
+  __shared__ __attribute__((aligned(16))) float Ds0[BQ];
+  __shared__ __attribute__((aligned(16))) float Ds1[BQ];
+  auto qbuf = [&](int p) -> unsigned char* { return p ? Qs1 : Qs0; };
+  auto gbuf = [&](int p) -> unsigned char* { return p ? Gs1 : Gs0; };
+  auto lbuf = [&](int p) -> float* { return p ? Ls1 : Ls0; };
+  auto dbuf = [&](int p) -> float* { return p ? Ds1 : Ds0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -153,42 +164,48 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  // LSE (pre-scaled by log2 e) and D of a query tile go through one VGPR of
-  // the first 2*BQ threads. A row without any visible key (LSE = -inf) has
-  // all its probabilities masked; a finite stand-in avoids inf - inf.
+  // LSE and D of a query tile go through one VGPR of the first 2*BQ threads:
+  // loaded raw at the start of the previous tile and only used (scaled and
+  // stored to LDS) at its end, so that no instruction of that tile waits for
+  // the load (loads complete in order, so such a wait would also wait for
+  // the tile copies issued just before it). A row without any visible key
+  // (LSE = -inf) has all its probabilities masked; a finite stand-in avoids
+  // inf - inf.
   float sreg = 0.f;
   auto load_stats = [&](int it) {
     if (tid < 2 * BQ) {
       const int q = it * BQ + (tid % BQ);
-      float x = 0.f;
-      if (q < N) x = (tid < BQ) ? Lg[q] * kLog2e : Dg[q];
-      sreg = (x == -INFINITY) ? 0.f : x;
+      sreg = 0.f;
+      if (q < N) sreg = (tid < BQ) ? Lg[q] : Dg[q];
     }
   };
-  auto store_stats = [&](int buf) {
-    if (tid < BQ) Ls[buf][tid] = sreg;
-    else if (tid < 2 * BQ) Ds[buf][tid - BQ] = sreg;
+  auto store_stats = [&](int p) {
+    if (tid < BQ) lbuf(p)[tid] = (sreg == -INFINITY) ? 0.f : sreg * kLog2e;
+    else if (tid < 2 * BQ) dbuf(p)[tid - BQ] = sreg;
   };
-  auto load_tiles = [&](int it, int buf) {
-    load_tile_lds<D, BQ, kBwdWaves>(rq, Qs[buf], it * BQ, wave, lane);
-    load_tile_lds<D, BQ, kBwdWaves>(rg, Gs[buf], it * BQ, wave, lane);
+  auto load_tiles = [&](int it, int p) {
+    load_tile_lds<D, BQ, kBwdWaves>(rq, qbuf(p), it * BQ, wave, lane);
+    load_tile_lds<D, BQ, kBwdWaves>(rg, gbuf(p), it * BQ, wave, lane);
   };
 
   if (qt_begin < qt_end) {
-    load_tiles(qt_begin, 0);
+    load_tiles(qt_begin, qt_begin & 1);
     load_stats(qt_begin);
-    store_stats(0);
-    __builtin_amdgcn_s_waitcnt(0);
+    store_stats(qt_begin & 1);
   }
+  // Unconditional, so that on every path into the loops below the K and V
+  // fragment loads above are known complete: the compiler places waits path
+  // by path, and would otherwise wait for them inside every tile, which at
+  // run time also waits for that tile's own prefetch copies.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // One query tile. FULL tiles (every key of the workgroup visible to every
   // query of the tile) run with no liveness test and no mask, so both query
   // sub-tiles sit in one basic block. Queries past N need no mask anywhere:
   // their Q and dO rows read as zero and their LSE and D as zero, so their P
   // meets a zero dO row and their dS is zero.
-  auto tile = [&](int it, auto full) {
+  auto tile = [&](int it, auto full, int buf) {
     constexpr bool FULL = decltype(full)::value;
-    const int buf = (it - qt_begin) & 1;
     // Tile it has landed everywhere; every wave is done with tile it-1, so
     // the other buffers are free for tile it+1.
     __syncthreads();
@@ -206,8 +223,8 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
       const bool need_mask = !FULL && ((key0 + 32 > kv_end) || (a.causal && key0 + 31 > q0));
 #pragma unroll
       for (int qs = 0; qs < QS; ++qs) {
-        const unsigned char* qt = Qs[buf] + qs * (32 / L::RPI) * L::GB;
-        const unsigned char* gt = Gs[buf] + qs * (32 / L::RPI) * L::GB;
+        const unsigned char* qt = qbuf(buf) + qs * (32 / L::RPI) * L::GB;
+        const unsigned char* gt = gbuf(buf) + qs * (32 / L::RPI) * L::GB;
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) s = Mfma<T>::mma32(*(const u32x4*)(qt + r_off[dc]), kf[dc], s);
@@ -217,8 +234,8 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int qi = qs * 32 + 8 * r4 + 4 * hh;
-          const f32x4 l4 = *(const f32x4*)&Ls[buf][qi];
-          const f32x4 d4 = *(const f32x4*)&Ds[buf][qi];
+          const f32x4 l4 = *(const f32x4*)&lbuf(buf)[qi];
+          const f32x4 d4 = *(const f32x4*)&dbuf(buf)[qi];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
@@ -239,10 +256,10 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
           const int rb = (2 * qs + c2) * L::rows16();
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const unsigned char* gp = Gs[buf] + rb + t_off[dt];
+            const unsigned char* gp = gbuf(buf) + rb + t_off[dt];
             const u32x2 g0 = lds_read_tr(gp), g1 = lds_read_tr(gp + L::half_step());
             dv[dt] = Mfma<T>::mma32(u32x4{g0.x, g0.y, g1.x, g1.y}, pf, dv[dt]);
-            const unsigned char* qp = Qs[buf] + rb + t_off[dt];
+            const unsigned char* qp = qbuf(buf) + rb + t_off[dt];
             const u32x2 q0v = lds_read_tr(qp), q1v = lds_read_tr(qp + L::half_step());
             dk[dt] = Mfma<T>::mma32(u32x4{q0v.x, q0v.y, q1v.x, q1v.y}, sf, dk[dt]);
           }
@@ -260,8 +277,15 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   int it_full = qt_end;
   if (blk_key0 + BK <= kv_end) it_full = a.causal ? max(qt_begin, (blk_key0 + BK - 1 + BQ - 1) / BQ) : qt_begin;
   it_full = min(it_full, qt_end);
-  for (int it = qt_begin; it < it_full; ++it) tile(it, Part{});
-  for (int it = it_full; it < qt_end; ++it) tile(it, Full{});
+  int it = qt_begin;
+  for (; it < it_full; ++it) tile(it, Part{}, it & 1);
+  // Full tiles in pairs of known parity (an odd first tile on its own).
+  if (it < qt_end && (it & 1)) tile(it++, Full{}, 1);
+  for (; it + 1 < qt_end; it += 2) {
+    tile(it, Full{}, 0);
+    tile(it + 1, Full{}, 1);
+  }
+  if (it < qt_end) tile(it, Full{}, 0);
 
   // dK^T / dV^T accumulators: lane = key, registers = d in runs of 4.
   if (my_key < N) {
@@ -311,8 +335,14 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   constexpr int DT = D / 32;
   constexpr int TB = L::bytes(BC);
 
-  __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TB];
+  // Double buffers of K and V as separate variables (see the dK/dV kernel);
+  // key tile j uses the buffers of parity j & 1.
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks0[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks1[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs0[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs1[TB];
+  auto kbuf = [&](int p) -> unsigned char* { return p ? Ks1 : Ks0; };
+  auto vbuf = [&](int p) -> unsigned char* { return p ? Vs1 : Vs0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -387,13 +417,13 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  auto load_k = [&](int j) { load_tile_lds<D, BC, kBwdWaves>(rk, Ks[j & 1], j * BC, wave, lane); };
-  auto load_v = [&](int j) { load_tile_lds<D, BC, kBwdWaves>(rv, Vs[j & 1], j * BC, wave, lane); };
-  auto compute_sdp = [&](int j, f32x16 (&s)[KT], f32x16 (&dp)[KT]) {
+  auto load_k = [&](int j, int p) { load_tile_lds<D, BC, kBwdWaves>(rk, kbuf(p), j * BC, wave, lane); };
+  auto load_v = [&](int j, int p) { load_tile_lds<D, BC, kBwdWaves>(rv, vbuf(p), j * BC, wave, lane); };
+  auto compute_sdp = [&](int p, f32x16 (&s)[KT], f32x16 (&dp)[KT]) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      const unsigned char* kp = Ks[j & 1] + kt * (32 / L::RPI) * L::GB;
-      const unsigned char* vp = Vs[j & 1] + kt * (32 / L::RPI) * L::GB;
+      const unsigned char* kp = kbuf(p) + kt * (32 / L::RPI) * L::GB;
+      const unsigned char* vp = vbuf(p) + kt * (32 / L::RPI) * L::GB;
       s[kt] = f32x16{};
       dp[kt] = f32x16{};
 #pragma unroll
@@ -404,27 +434,27 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   };
 
   if (ntiles > 0) {
-    load_k(0);
-    load_v(0);
+    load_k(0, 0);
+    load_v(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
   }
 
   // Tile j: S^T/dP^T, then dS and dQ. Full tiles (no causal mask for any
   // row of the workgroup) run with no liveness test.
-  auto tile = [&](int j, auto full) {
+  auto tile = [&](int j, auto full, int par) {
     constexpr bool FULL = decltype(full)::value;
     // Every wave is done with tile j-1, so its buffers take tile j+1.
     __syncthreads();
     if (FULL || j + 1 < ntiles) {
-      load_k(j + 1);
-      load_v(j + 1);
+      load_k(j + 1, par ^ 1);
+      load_v(j + 1, par ^ 1);
     }
     if (FULL || j < w_tiles) {
       // Full tiles: raise this wave's issue priority while it runs its MFMA
       // chains, so the SIMD's other waves fill the gaps around them.
       if constexpr (FULL) __builtin_amdgcn_s_setprio(1);
       f32x16 s_cur[KT], p_cur[KT];
-      compute_sdp(j, s_cur, p_cur);
+      compute_sdp(par, s_cur, p_cur);
       const int t0 = j * BC;
       const bool need_mask = !FULL && a.causal && t0 + BC - 1 > wq0;
 #pragma unroll
@@ -447,7 +477,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
           const int rb = (2 * kt + c2) * L::rows16();
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const unsigned char* kp = Ks[j & 1] + rb + t_off[dt];
+            const unsigned char* kp = kbuf(par) + rb + t_off[dt];
             const u32x2 k0 = lds_read_tr(kp), k1 = lds_read_tr(kp + L::half_step());
             dq[dt] = Mfma<T>::mma32(u32x4{k0.x, k0.y, k1.x, k1.y}, sf, dq[dt]);
           }
@@ -467,11 +497,11 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   n_full = min(n_full, ntiles - 1);
   int j = 0;
   for (; j + 1 < n_full; j += 2) {
-    tile(j, Full{});
-    tile(j + 1, Full{});
+    tile(j, Full{}, 0);
+    tile(j + 1, Full{}, 1);
   }
-  for (; j < n_full; ++j) tile(j, Full{});
-  for (; j < ntiles; ++j) tile(j, Part{});
+  for (; j < n_full; ++j) tile(j, Full{}, j & 1);
+  for (; j < ntiles; ++j) tile(j, Part{}, j & 1);
 
   if (my_q < N) {
     uint16_t* dQg = (uint16_t*)a.dq + head_off + (size_t)my_q * D;

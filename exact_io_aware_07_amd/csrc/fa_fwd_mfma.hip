@@ -69,8 +69,16 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   constexpr int DT = D / 32;                    // 32-wide d tiles of O^T
   constexpr int TB = L::bytes(BC);              // bytes per K or V tile
 
-  __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TB];
+  // Two buffers each of K and V, as four separate variables: the compiler
+  // can then tell a copy into one buffer from reads of the other and does
+  // not make the reads wait for the copy (it would with one array of two).
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks0[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks1[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs0[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs1[TB];
+  // Buffer of parity p; p is a compile-time constant in the main loop.
+  auto kbuf = [&](int p) -> unsigned char* { return p ? Ks1 : Ks0; };
+  auto vbuf = [&](int p) -> unsigned char* { return p ? Vs1 : Vs0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,13 +133,13 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   int k_off[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) k_off[dc] = L::off(ql, 2 * dc + hh);
-  auto compute_s = [&](int buf, f32x16 (&s)[KT]) {
+  auto compute_s = [&](const unsigned char* kb, f32x16 (&s)[KT]) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       s[kt] = f32x16{};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const u32x4 kf = *(const u32x4*)&Ks[buf][kt * (32 / L::RPI) * L::GB + k_off[dc]];
+        const u32x4 kf = *(const u32x4*)&kb[kt * (32 / L::RPI) * L::GB + k_off[dc]];
         s[kt] = Mfma<T>::mma32(kf, qf[dc], s[kt]);
       }
     }
@@ -145,12 +153,12 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
 
   f32x16 s_a[KT], s_b[KT];
   if (ntiles > 0) {
-    load_tile(rk, Ks[0], 0);
-    load_tile(rk, Ks[1], 1);
-    load_tile(rv, Vs[0], 0);
+    load_tile(rk, Ks0, 0);
+    load_tile(rk, Ks1, 1);
+    load_tile(rv, Vs0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (w_tiles > 0) compute_s(0, s_a);
+    if (w_tiles > 0) compute_s(Ks0, s_a);
   }
 
   // One tile of the pipeline: S of tile j+1 into s_nxt, softmax and P V of
@@ -160,14 +168,14 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   // in one basic block and the scheduler can interleave MFMA and VALU work.
   // Other tiles (the causal diagonal, the padded or ragged end) take the
   // general path with per-wave liveness and masking.
-  auto tile = [&](int j, f32x16 (&s_cur)[KT], f32x16 (&s_nxt)[KT], auto full) {
+  auto tile = [&](int j, f32x16 (&s_cur)[KT], f32x16 (&s_nxt)[KT], auto full, int par) {
     constexpr bool FULL = decltype(full)::value;
     // Every wave has finished tile j-1: the K buffer of tile j and the V
     // buffer of tile j-1 are free. Loads past the last tile read inside the
     // head, or zeros past the resource end, and are never used.
     __syncthreads();
-    if (FULL || j + 2 < ntiles) load_tile(rk, Ks[j & 1], j + 2);
-    if (FULL || j + 1 < ntiles) load_tile(rv, Vs[(j + 1) & 1], j + 1);
+    if (FULL || j + 2 < ntiles) load_tile(rk, kbuf(par), j + 2);
+    if (FULL || j + 1 < ntiles) load_tile(rv, vbuf(par ^ 1), j + 1);
     const bool live = FULL || j < w_tiles;
     if (live) {
       if constexpr (!FULL) {
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
       __builtin_amdgcn_iglp_opt(0);
       __builtin_amdgcn_s_setprio(1);
     }
-    if (FULL || j + 1 < w_tiles) compute_s((j + 1) & 1, s_nxt);
+    if (FULL || j + 1 < w_tiles) compute_s(kbuf(par ^ 1), s_nxt);
 
       const float mref2 = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
       float lsum = 0.f;
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
 
       // O^T += V^T P^T, 16 keys per MFMA. Rows kt*32 + c2*16 (+8) of the V
       // tile start whole groups, so they only move the group base.
-      const unsigned char* vb = Vs[j & 1];
+      const unsigned char* vb = vbuf(par);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -262,11 +270,11 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   n_full = min(n_full, ntiles - 1) & ~1;
   int j = 0;
   for (; j < n_full; j += 2) {
-    tile(j, s_a, s_b, Full{});
-    tile(j + 1, s_b, s_a, Full{});
+    tile(j, s_a, s_b, Full{}, 0);
+    tile(j + 1, s_b, s_a, Full{}, 1);
   }
   for (; j < ntiles; ++j) {
-    tile(j, s_a, s_b, Part{});
+    tile(j, s_a, s_b, Part{}, j & 1);
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) s_a[kt] = s_b[kt];
   }
