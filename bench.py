@@ -50,6 +50,31 @@ def fwd_flops(w) -> float:
     return 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
 
 
+def compulsory_bytes(w, backward: bool) -> float:
+    """Bytes the pass must move to or from HBM at least: forward reads Q, K, V
+    and writes O and LSE; backward reads Q, K, V, O, dO, LSE (and D) and
+    writes dQ, dK, dV (and D)."""
+    e = 4 if w.dtype == "fp32" else 2
+    per_row = (8 * w.d * e + 8) if backward else (4 * w.d * e + 4)
+    return float(w.B * w.H * w.N * per_row)
+
+
+def device_info(torch) -> dict:
+    """Name, CU count and the runtime's peak clock of device 0."""
+    import ctypes
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": p.gcnArchName, "cus": p.multi_processor_count,
+            "l2_bytes": p.L2_cache_size}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) == 0:  # hipDeviceAttributeClockRate
+            info["peak_clock_mhz"] = khz.value / 1000.0
+    except OSError:
+        pass
+    return info
+
+
 def kernel_work(name: str, w) -> float:
     """Algorithmic FLOPs (mfma kernels) or bytes (hbm kernels) per launch."""
     half = 0.5 if w.causal else 1.0
@@ -138,6 +163,21 @@ def run_gpu(args):
         torch.cuda.synchronize()
         avg_ms[n] = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step; kernels (ms) {avg_ms}")
+    # Cold caches: before each of up to 50 steps, write a 512 MiB scratch
+    # buffer (more than L2 and the 256 MB MALL together), then time the step
+    # alone with two events; the median step is reported.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for i in range(min(args.steps, 50)):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        cold.append((e0, e1))
+    torch.cuda.synchronize()
+    cold_ms = statistics.median(a.elapsed_time(b) for a, b in cold)
+    del flush
 
     f_fwd = fwd_flops(w)
     f_bwd = 2.5 * f_fwd
@@ -186,6 +226,9 @@ def run_gpu(args):
         "bwd_tflops": f_bwd / ((avg_ms["dq"] + avg_ms["dkdv"]) * 1e-3) / 1e12,
         "kernels": kernels,
         "kernel_sum_us": sum(avg_ms.values()) * 1e3,
+        "cold_cache": {"ms_per_step": cold_ms, "tflops": (f_fwd + f_bwd) / (cold_ms * 1e-3) / 1e12,
+                       "steps": len(cold), "flush_bytes": 512 << 20},
+        "device": device_info(torch),
         "roofline": roof,
     }
     if not args.no_extra:
@@ -212,15 +255,24 @@ def extra_configs(torch, W, iters: int = 10):
         while time.perf_counter() - t_w < 0.3:
             fn()
             torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(iters):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / iters
+        # batches of `iters` calls between two events, until at least 50
+        # calls and 100 ms; the median batch gives the time per call
+        batches, total_ms = [], 0.0
+        while len(batches) * iters < 50 or total_ms < 100.0:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(iters):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            batches.append(s.elapsed_time(e) / iters)
+            total_ms += batches[-1] * iters
+        ms = statistics.median(batches)
         rate = flops / (ms * 1e-3)
-        entry = {"ms": ms, "tflops": rate / 1e12, "pct_of_bf16_peak": 100 * rate / PEAK_BF16_FLOPS}
+        gbps = compulsory_bytes(w, w.backward) / (ms * 1e-3) / 1e9
+        entry = {"ms": ms, "tflops": rate / 1e12, "pct_of_bf16_peak": 100 * rate / PEAK_BF16_FLOPS,
+                 "calls": len(batches) * iters, "compulsory_gbps": gbps,
+                 "pct_of_hbm_peak": 100 * gbps * 1e9 / PEAK_HBM_BYTES}
         if w.kv_len_range is not None:
             eff = 4.0 * w.H * w.N * w.d * float(inp["kv_len"].sum().item())
             entry["tflops_effective_kv_len"] = eff / (ms * 1e-3) / 1e12
@@ -264,8 +316,14 @@ def cpu_baseline(target_s: float = 12.0):
         threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
     except Exception:
         threads = None
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s",
-            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "cores": threads or os.cpu_count(), "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"{w.name}: forward+backward of {n} of {len(heads_all)} heads "
                       f"(fp64, materialised S), median of {len(times)} passes, {elapsed:.2f} s each",
             "seconds": elapsed}

@@ -5,8 +5,15 @@
         --copy-fetch CSV --copy-write CSV --copy-bytes N --workload NAME \
         --cmd "..." --out-md FILE.md --out-json profiles/traffic.json
 
+    python -m exact_io_aware_07_amd.profiling counters CSV [CSV ...] --workload NAME \
+        --cmd "..." --out FILE.md
+
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a short
-markdown table. ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
+markdown table. ``counters`` merges ``--pmc`` passes (one CSV each) into one
+table per kernel with ratios that need no normalisation across counter
+instances: share of wave cycles issuing VALU or waiting, LDS bank-conflict
+cycles per LDS-active cycle, L2 hit rate, and VALU / transcendental / LDS
+instructions per MFMA instruction. ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
 WRITE_SIZE, KiB per dispatch) into HBM bytes per launch, each counter scaled
 by what it reads for a plain device copy of known size, and records the hash
 of the kernel sources the counters were taken on, so a stale figure is
@@ -78,6 +85,49 @@ def stats_md(csv_path: str, cmd: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+# derived ratio -> (numerator, denominator)
+RATIOS = {
+    "VALU issuing / wave cycles": ("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+    "LDS issuing / wave cycles": ("SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
+    "waiting on a counter / wave cycles": ("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    "LDS bank-conflict / LDS-active cycles": ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+    "VALU insts / MFMA inst": ("SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
+    "transcendental insts / MFMA inst": ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA"),
+    "LDS insts / MFMA inst": ("SQ_INSTS_LDS", "SQ_INSTS_MFMA"),
+}
+
+
+def counters_md(paths: List[str], workload: str, cmd: str) -> str:
+    per: Dict[str, Dict[str, float]] = collections.defaultdict(dict)
+    for path in paths:
+        vals: Dict[tuple, List[float]] = collections.defaultdict(list)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                short = short_name(r["Kernel_Name"])
+                if short in KERNELS:
+                    vals[(short, r["Counter_Name"])].append(float(r["Counter_Value"]))
+        for (short, c), v in vals.items():
+            per[short][c] = sum(v) / len(v)
+    lines = ["# Shader counters per kernel (rocprofv3 --pmc)", "", f"Workload: `{workload}`.", "",
+             "Commands (one pass each):", "", "```", cmd, "```", "",
+             "| kernel | " + " | ".join(RATIOS) + " | L2 hit rate |",
+             "|---|" + "---|" * (len(RATIOS) + 1)]
+    for short in sorted(per):
+        c = per[short]
+        cells = []
+        for num, den in RATIOS.values():
+            cells.append(f"{c[num] / c[den]:.3f}" if num in c and c.get(den) else "—")
+        hit = c.get("TCC_HIT_sum", c.get("TCC_HIT"))
+        miss = c.get("TCC_MISS_sum", c.get("TCC_MISS"))
+        cells.append(f"{hit / (hit + miss):.3f}" if hit is not None and miss is not None and hit + miss > 0 else "—")
+        lines.append(f"| `{short}` | " + " | ".join(cells) + " |")
+    lines += ["", "Raw means per dispatch:", "", "| kernel | counter | value |", "|---|---|---|"]
+    for short in sorted(per):
+        for cname, v in sorted(per[short].items()):
+            lines.append(f"| `{short}` | {cname} | {v:.4g} |")
+    return "\n".join(lines) + "\n"
+
+
 def traffic(args) -> None:
     ff = _copy_factor(args.copy_fetch, "FETCH_SIZE", args.copy_bytes)
     fw = _copy_factor(args.copy_write, "WRITE_SIZE", args.copy_bytes)
@@ -119,10 +169,18 @@ def main() -> None:
     for name in ("fetch", "write", "copy_fetch", "copy_write", "workload", "cmd", "out_md", "out_json"):
         t.add_argument("--" + name.replace("_", "-"), dest=name, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.what == "stats":
         with open(a.out, "w") as fh:
             fh.write(stats_md(a.csv, a.cmd))
+    elif a.what == "counters":
+        with open(a.out, "w") as fh:
+            fh.write(counters_md(a.csv, a.workload, a.cmd))
     else:
         traffic(a)
 
