@@ -6,5 +6,6 @@ this package. The library (``exact_io_aware_07_amd``) never imports it and
 shares no code with it; the two meet only at the seeded input generator.
 """
 from .attention import attn_bwd64, attn_bwd64_sampled, attn_fwd64, attn_probs64, visible_mask  # noqa: F401
-from .brute import brute_head_forward, brute_head_grad_fd, brute_loss  # noqa: F401
+from .brute import brute_head_forward, brute_head_grad_fd, brute_head_part, brute_loss  # noqa: F401
 from .memory import score_matrix_bytes  # noqa: F401
+from .split import attn_part64, merge64  # noqa: F401

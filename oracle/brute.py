@@ -78,3 +78,28 @@ def brute_head_grad_fd(q, k, v, do, scale: float, causal: bool = False,
                 g[i][c] = (lp - lm) / (2.0 * step)
         grads[name] = g
     return grads["q"], grads["k"], grads["v"]
+
+
+def brute_head_part(q, k, v, scale: float, causal: bool = False, q_pos0: int = 0,
+                    k_pos0: int = 0) -> Tuple[Matrix, List[float]]:
+    """One head, queries at global positions q_pos0 + i against keys at
+    global positions k_pos0 + j (causal hides later key positions); returns
+    (O rows, LSE per row), O = 0 and LSE = -inf for a row with no visible key."""
+    q, k, v = _as_rows(q), _as_rows(k), _as_rows(v)
+    dv = len(v[0]) if v else len(q[0])
+    o_rows: Matrix = []
+    lse: List[float] = []
+    for i, qi in enumerate(q):
+        keys = [j for j in range(len(k)) if (not causal or k_pos0 + j <= q_pos0 + i)]
+        if not keys:
+            o_rows.append([0.0] * dv)
+            lse.append(-math.inf)
+            continue
+        s = [scale * math.fsum(qi[c] * k[j][c] for c in range(len(qi))) for j in keys]
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        tot = math.fsum(e)
+        o_rows.append([math.fsum(e[t] * v[j][c] for t, j in enumerate(keys)) / tot
+                       for c in range(dv)])
+        lse.append(mx + math.log(tot))
+    return o_rows, lse
