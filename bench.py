@@ -233,6 +233,7 @@ def run_gpu(args):
     }
     if not args.no_extra:
         out["extra"] = extra_configs(torch, W)
+        out["extra"][W.FEW_HEADS.name] = split_config(torch, W)
     return out
 
 
@@ -280,6 +281,44 @@ def extra_configs(torch, W, iters: int = 10):
         log(f"[bench] extra {w.name}: {entry}")
         del inp, o, lse
     return res
+
+
+def split_config(torch, W, num_splits: int = 2):
+    """The few-heads causal shape with the plain forward and with the
+    key-split forward (num_splits parts, one launch, then one merge launch)."""
+    from exact_io_aware_07_amd import fa_fwd, fa_fwd_split, fa_fwd_split_workspace_bytes
+    w = W.FEW_HEADS
+    inp = W.make_inputs(w)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(fa_fwd_split_workspace_bytes(w.B, w.H, w.N, w.d, num_splits), 16),
+                     dtype=torch.uint8, device="cuda")
+    runs = {"fwd": lambda: fa_fwd(q, k, v, o, lse, w.scale, w.causal),
+            "split": lambda: fa_fwd_split(q, k, v, o, lse, w.scale, w.causal, None, num_splits, ws)}
+    flops = fwd_flops(w)
+    entry = {"num_splits": num_splits, "workspace_bytes": ws.numel()}
+    for name, fn in runs.items():
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.3:
+            fn()
+            torch.cuda.synchronize()
+        batches = []
+        while len(batches) < 5 or sum(batches) * 10 < 100.0:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(10):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            batches.append(s.elapsed_time(e) / 10)
+        ms = statistics.median(batches)
+        entry[f"{name}_ms"] = ms
+        entry[f"{name}_tflops"] = flops / (ms * 1e-3) / 1e12
+        entry[f"{name}_pct_of_bf16_peak"] = 100 * flops / (ms * 1e-3) / PEAK_BF16_FLOPS
+    entry["split_speedup"] = entry["fwd_ms"] / entry["split_ms"]
+    log(f"[bench] extra {w.name}: {entry}")
+    return entry
 
 
 def cpu_baseline(target_s: float = 12.0):

@@ -48,6 +48,25 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Key split of a key-split forward: keys per part (a multiple of the
+// kernels' 64-key tile) and the number of parts that covers N.
+void split_plan(int N, int num_splits, int* ksplit, int* parts) {
+  int ks = (N + num_splits - 1) / num_splits;
+  ks = ((ks + 63) / 64) * 64;
+  if (ks < 64) ks = 64;
+  *ksplit = ks;
+  *parts = N > 0 ? (N + ks - 1) / ks : 1;
+}
+
+size_t split_workspace(int B, int H, int N, int d, int parts) {
+  if (parts <= 1) return 0;
+  return (size_t)parts * (size_t)B * H * N * (size_t)(d + 1) * sizeof(float);
+}
+
+// Positions of a partial step are bounded so that every sum of a position
+// difference and a row index stays inside a 32-bit int.
+constexpr int kMaxPos = 1 << 29;
+
 }  // namespace
 
 extern "C" {
@@ -65,7 +84,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return FA_ERR_INVALID_ARG;
   if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
 
-  fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal};
+  fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = (in_dtype == FA_F32) ? fa::launch_fwd_f32(a, s)
                                       : fa::launch_fwd_mfma(a, elem(in_dtype), elem(o_dtype), s);
@@ -141,6 +160,104 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const 
   if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
   return launch_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, dsum, kv_len, B, H, N, d, scale,
                     causal, stream, dtype, (int)fa::BwdStage::DQ);
+}
+
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int q_pos0,
+                   int k_pos0, const int* kv_len, void* stream, int in_dtype) {
+  int st = check_scalars(B, H, Nq, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (Nk < 0) return FA_ERR_INVALID_ARG;
+  if ((long long)Nk * d * 4 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if (q_pos0 <= -kMaxPos || q_pos0 >= kMaxPos || k_pos0 <= -kMaxPos || k_pos0 >= kMaxPos)
+    return FA_ERR_INVALID_ARG;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * Nq == 0) return FA_OK;
+  if (!q || !o_part || !lse_part) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o_part) || !aligned4(lse_part)) return FA_ERR_INVALID_ARG;
+  // With no keys, k and v are never read and may be NULL.
+  if (Nk > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+
+  fa::FwdArgs a{q, k, v, o_part, lse_part, kv_len, B, H, Nq, d, scale, causal,
+                Nk, q_pos0, k_pos0, 1, Nk, 0, 0};
+  hipError_t e = fa::launch_fwd_mfma_general(a, elem(in_dtype), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b, void* o,
+             float* lse, long long rows, int d, void* stream, int o_dtype) {
+  if (rows < 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!dtype_ok(o_dtype)) return FA_ERR_UNSUPPORTED;
+  if (rows / 8 + 1 > kMaxBlocks) return FA_ERR_INVALID_ARG;
+  if (rows == 0) return FA_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o) || !aligned4(lse_a) || !aligned4(lse_b) ||
+      !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  fa::MergeArgs m{};
+  m.o[0] = o_a;
+  m.o[1] = o_b;
+  m.lse[0] = lse_a;
+  m.lse[1] = lse_b;
+  m.nparts = 2;
+  m.out_o = o;
+  m.out_lse = lse;
+  m.rows = rows;
+  hipError_t e = fa::launch_merge(m, d, elem(o_dtype), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int num_splits) {
+  if (B < 0 || H < 0 || N < 0 || d < 0 || num_splits < 1 || num_splits > fa::kMaxMergeParts) return 0;
+  int ks, parts;
+  split_plan(N, num_splits, &ks, &parts);
+  return split_workspace(B, H, N, d, parts);
+}
+
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, const int* kv_len, int num_splits,
+                 void* workspace, size_t workspace_bytes, void* stream, int in_dtype,
+                 int o_dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > fa::kMaxMergeParts) return FA_ERR_INVALID_ARG;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  int ks, parts;
+  split_plan(N, num_splits, &ks, &parts);
+  hipStream_t s = (hipStream_t)stream;
+  if (parts == 1) {
+    fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0};
+    hipError_t e = fa::launch_fwd_mfma(a, elem(in_dtype), elem(o_dtype), s);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
+  if (!workspace || !aligned16(workspace) || workspace_bytes < split_workspace(B, H, N, d, parts))
+    return FA_ERR_WORKSPACE;
+  float* wo = (float*)workspace;
+  const long long so = (long long)B * H * N * d;
+  const long long sl = (long long)B * H * N;
+  float* wl = wo + parts * so;
+  fa::FwdArgs a{q, k, v, wo, wl, kv_len, B, H, N, d, scale, causal, N, 0, 0, parts, ks, so, sl};
+  hipError_t e = fa::launch_fwd_mfma_general(a, elem(in_dtype), s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  fa::MergeArgs m{};
+  for (int p = 0; p < parts; ++p) {
+    m.o[p] = wo + p * so;
+    m.lse[p] = wl + p * sl;
+  }
+  m.nparts = parts;
+  m.out_o = o;
+  m.out_lse = lse;
+  m.rows = sl;
+  e = fa::launch_merge(m, d, elem(o_dtype), s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_strerror(int status) {

@@ -60,7 +60,11 @@ struct FwdTile {
   static constexpr int OCC = (D == 64) ? 3 : 2;  // waves per SIMD the registers allow
 };
 
-template <typename T, int D, bool OUT_F32>
+// GEN: the general form (key count, positions and key split from the
+// arguments); without it they are folded to the plain forward's (Nk = N,
+// equal positions, one split), so that path compiles as if they did not
+// exist.
+template <typename T, int D, bool OUT_F32, bool GEN>
 __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(FwdArgs a) {
   using L = TileLayout<D>;
   constexpr int BC = FwdTile<D>::BC;
@@ -88,29 +92,43 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
 
   const int N = a.N;
   const int nqb = (N + kBR - 1) / kBR;
-  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nqb, a.B * a.H, a.causal, FwdTile<D>::OCC);
+  // The key split is the outermost grid index; inside a split, blocks are
+  // placed as for the whole forward.
+  const int per_split = a.B * a.H * nqb;
+  const int split = GEN ? blockIdx.x / per_split : 0;
+  const BlockPick pk = pick_block(blockIdx.x - split * per_split, per_split, nqb, a.B * a.H, a.causal,
+                                  FwdTile<D>::OCC);
   const int bh = pk.bh;
   const int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;  // causal: last block has most work
   const int b = bh / a.H;
 
-  const size_t head_off = (size_t)bh * N * D;
-  int kv_end = N;
-  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
+  const size_t head_off = (size_t)bh * N * D;          // Q and O
+  const int Nk = GEN ? a.Nk : N;
+  const size_t head_k = (size_t)bh * Nk * D;           // K and V
+  const int k_lo = GEN ? split * a.ksplit : 0;         // this split's keys: [k_lo, k_hi)
+  int kv_end = GEN ? min(k_lo + a.ksplit, Nk) : N;     // keys visible at all (exclusive)
+  if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), kv_end);
+  // causal: key j visible to query i iff j <= i + delta
+  const int delta = GEN ? a.q_pos0 - a.k_pos0 : 0;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + head_off, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + head_off, (uint32_t)kv_end * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + head_off, (uint32_t)kv_end * D * 2);
+  const uint32_t kv_bytes = (uint32_t)max(kv_end, 0) * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + head_k, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + head_k, kv_bytes);
 
   const int q_blk0 = qb * kBR;
   const int q_blk_last = min(q_blk0 + kBR, N) - 1;
   int kv_lim = kv_end;  // keys the workgroup needs (exclusive)
-  if (a.causal) kv_lim = min(kv_lim, q_blk_last + 1);
-  const int ntiles = (kv_lim + BC - 1) / BC;
+  if (a.causal) kv_lim = min(kv_lim, q_blk_last + delta + 1);
+  // Tiles are counted from this split's first tile jb (k_lo is a multiple of
+  // the tile width); tile t holds keys [(jb + t) * BC, (jb + t + 1) * BC).
+  const int jb = k_lo / BC;
+  const int ntiles = max((kv_lim + BC - 1) / BC - jb, 0);
 
   const int wq0 = q_blk0 + wave * 32;
   const int my_q = wq0 + ql;
   int w_lim = kv_end;  // keys this wave needs (exclusive)
-  if (a.causal) w_lim = min(w_lim, min(wq0 + 31, N - 1) + 1);
-  const int w_tiles = (w_lim + BC - 1) / BC;  // tiles this wave computes
+  if (a.causal) w_lim = min(w_lim, min(wq0 + 31, N - 1) + delta + 1);
+  const int w_tiles = max((max(w_lim, 0) + BC - 1) / BC - jb, 0);  // tiles this wave computes
 
   u32x4 qf[DC];
 #pragma unroll
@@ -123,8 +141,8 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   float l_run = 0.f;        // running sum over this half's keys, against m_ref
   const float sl2 = a.scale * kLog2e;
 
-  auto load_tile = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int j) {
-    load_tile_lds<D, BC, kWaves>(r, dst, j * BC, wave, lane);
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int t) {
+    load_tile_lds<D, BC, kWaves>(r, dst, (jb + t) * BC, wave, lane);
   };
 
   // K fragment (A of S^T): row kt*32 + ql, chunk 2*dc + hh. The row's place
@@ -179,15 +197,15 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
     const bool live = FULL || j < w_tiles;
     if (live) {
       if constexpr (!FULL) {
-        const int t0 = j * BC;
-        const bool need_mask = (t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0);
+        const int t0 = (jb + j) * BC;
+        const bool need_mask = (t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0 + delta);
         if (need_mask) {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              const bool vis = key < kv_end && (!a.causal || key <= my_q);
+              const bool vis = key < kv_end && (!a.causal || key <= my_q + delta);
               if (!vis) s_cur[kt][r] = -INFINITY;
             }
           }
@@ -266,8 +284,8 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   // Tiles fully visible to every row of the workgroup, and followed by a
   // further tile, form the branch-free main loop (an even count, so the two
   // S arrays swap roles without copies).
-  int n_full = (a.causal ? min(kv_end, q_blk0 + 1) : kv_end) / BC;
-  n_full = min(n_full, ntiles - 1) & ~1;
+  const int n_vis = (a.causal ? min(kv_end, q_blk0 + delta + 1) : kv_end) / BC - jb;
+  const int n_full = max(min(n_vis, ntiles - 1), 0) & ~1;
   int j = 0;
   for (; j < n_full; j += 2) {
     tile(j, s_a, s_b, Full{}, 0);
@@ -290,33 +308,33 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
         const float o0 = oacc[dt][4 * r4 + 0] * inv, o1 = oacc[dt][4 * r4 + 1] * inv;
         const float o2 = oacc[dt][4 * r4 + 2] * inv, o3 = oacc[dt][4 * r4 + 3] * inv;
         if constexpr (OUT_F32) {
-          float* Og = (float*)a.o + head_off;
+          float* Og = (float*)a.o + (GEN ? split * a.o_split_stride : 0) + head_off;
           *(f32x4*)(Og + (size_t)my_q * D + d0) = f32x4{o0, o1, o2, o3};
         } else {
-          uint16_t* Og = (uint16_t*)a.o + head_off;
+          uint16_t* Og = (uint16_t*)a.o + (GEN ? split * a.o_split_stride : 0) + head_off;
           *(u32x2*)(Og + (size_t)my_q * D + d0) = u32x2{Mfma<T>::pack(o0, o1), Mfma<T>::pack(o2, o3)};
         }
       }
     }
     if (hh == 0) {
-      a.lse[(size_t)bh * N + my_q] =
+      a.lse[(GEN ? split * a.lse_split_stride : 0) + (size_t)bh * N + my_q] =
           (l_tot > 0.f) ? m_ref * a.scale + fast_log2(l_tot) * kLn2 : -INFINITY;
     }
   }
 }
 
-template <typename T, int D, bool OF>
+template <typename T, int D, bool OF, bool GEN>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const long nqb = (a.N + kBR - 1) / kBR;
-  const long total = (long)a.B * a.H * nqb;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, OF>), dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  const long total = (long)a.B * a.H * nqb * (GEN ? a.nsplit : 1);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, OF, GEN>), dim3((unsigned)total), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const FwdArgs& a, bool of, hipStream_t s) {
-  if (a.d == 128) return of ? launch<T, 128, true>(a, s) : launch<T, 128, false>(a, s);
-  return of ? launch<T, 64, true>(a, s) : launch<T, 64, false>(a, s);
+  if (a.d == 128) return of ? launch<T, 128, true, false>(a, s) : launch<T, 128, false, false>(a, s);
+  return of ? launch<T, 64, true, false>(a, s) : launch<T, 64, false, false>(a, s);
 }
 
 }  // namespace
@@ -325,6 +343,12 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, Elem in, Elem out, hipStream_t s) {
   const bool of = (out == Elem::F32);
   if (in == Elem::BF16) return launch_t<BF16>(a, of, s);
   return launch_t<F16>(a, of, s);
+}
+
+hipError_t launch_fwd_mfma_general(const FwdArgs& a, Elem in, hipStream_t s) {
+  if (in == Elem::BF16)
+    return a.d == 128 ? launch<BF16, 128, true, true>(a, s) : launch<BF16, 64, true, true>(a, s);
+  return a.d == 128 ? launch<F16, 128, true, true>(a, s) : launch<F16, 64, true, true>(a, s);
 }
 
 }  // namespace fa

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 enum class Elem { F32 = 0, F16 = 1, BF16 = 2 };
@@ -16,9 +18,16 @@ struct FwdArgs {
   void* o;
   float* lse;
   const int* kv_len;  // device [B] or nullptr
-  int B, H, N, d;
+  int B, H, N, d;     // N: query rows per head
   float scale;
   int causal;
+  // Keys and positions (the plain forward: Nk = N, both offsets 0, one split
+  // of N keys, strides 0). Key j is visible to query i under the causal
+  // mask when k_pos0 + j <= q_pos0 + i.
+  int Nk;
+  int q_pos0, k_pos0;
+  int nsplit, ksplit;  // split s streams keys [s * ksplit, (s + 1) * ksplit)
+  long long o_split_stride, lse_split_stride;  // elements between splits' outputs
 };
 
 struct BwdArgs {
@@ -41,6 +50,9 @@ struct BwdArgs {
 // Launchers return hipSuccess or the launch error. Arguments are validated
 // by the caller.
 hipError_t launch_fwd_mfma(const FwdArgs& a, Elem in, Elem out, hipStream_t s);
+// The general form (Nk, positions and key split from the arguments), fp32
+// output; the plain forward above ignores those fields.
+hipError_t launch_fwd_mfma_general(const FwdArgs& a, Elem in, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 // Backward stages, launched in this order when several are asked for: the
 // stand-alone D_i = rowsum(dO * O), then dQ (which also forms D_i for its
@@ -48,6 +60,20 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 enum class BwdStage { DSUM = 1, DKDV = 2, DQ = 4, ALL = 7 };
 hipError_t launch_bwd_mfma(const BwdArgs& a, Elem t, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
+
+// Merge of partial results (fp32 O [rows][d] and LSE [rows] per part) into
+// out_o (fp32, fp16 or bf16) and out_lse. out_o / out_lse may alias part 0
+// when the output is fp32.
+constexpr int kMaxMergeParts = 16;
+struct MergeArgs {
+  const float* o[kMaxMergeParts];
+  const float* lse[kMaxMergeParts];
+  int nparts;
+  void* out_o;
+  float* out_lse;
+  long long rows;
+};
+hipError_t launch_merge(const MergeArgs& a, int d, Elem out, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Device helpers (gfx950).

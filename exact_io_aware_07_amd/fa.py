@@ -19,7 +19,8 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_dsum", "fa_bwd_dkdv",
-           "fa_bwd_dq", "fa_strerror")
+           "fa_bwd_dq", "fa_fwd_partial", "fa_merge", "fa_fwd_split_workspace_bytes",
+           "fa_fwd_split", "fa_strerror")
 
 _DTYPE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib: Optional[ctypes.CDLL] = None
@@ -52,6 +53,14 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_dkdv.restype = i
     L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
     L.fa_bwd_dq.restype = i
+    L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, i]
+    L.fa_fwd_partial.restype = i
+    L.fa_merge.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_longlong, i, vp, i]
+    L.fa_merge.restype = i
+    L.fa_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_fwd_split_workspace_bytes.restype = sz
+    L.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp, i, i]
+    L.fa_fwd_split.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -182,6 +191,73 @@ def fa_bwd_dq(q, k, v, o, dout, lse, dsum, dq, scale: float, causal: bool = Fals
                          _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_dq")
+
+
+def fa_fwd_partial(q, k, v, o_part, lse_part, scale: float, causal: bool = False,
+                   q_pos0: int = 0, k_pos0: int = 0, kv_len=None, stream=None) -> None:
+    """Enqueue attention of q [B, H, Nq, d] (positions q_pos0 + i) over k, v
+    [B, H, Nk, d] (positions k_pos0 + j): o_part fp32 [B, H, Nq, d], lse_part
+    fp32 [B, H, Nq]."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _check_tensor("q", q, q.shape)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, H, Nk, d), q.dtype)
+    _check_tensor("o_part", o_part, (B, H, Nq, d), torch.float32)
+    _check_tensor("lse_part", lse_part, (B, H, Nq), torch.float32)
+    st = lib().fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, H, Nq,
+                              Nk, d, float(scale), int(bool(causal)), int(q_pos0), int(k_pos0),
+                              _kv(kv_len, B), _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_partial")
+
+
+def fa_merge(o_a, lse_a, o_b, lse_b, o, lse, stream=None) -> None:
+    """Enqueue (o, lse) = merge((o_a, lse_a), (o_b, lse_b)): o_a, o_b fp32
+    [..., d]; lse_a, lse_b, lse fp32 [...]; o [..., d] fp32/fp16/bf16 (may be
+    o_a, with lse = lse_a, when fp32)."""
+    d = o_a.shape[-1]
+    rows = lse_a.numel()
+    for name, t in (("o_a", o_a), ("o_b", o_b)):
+        _check_tensor(name, t, o_a.shape, torch.float32)
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b), ("lse", lse)):
+        _check_tensor(name, t, lse_a.shape, torch.float32)
+    _check_tensor("o", o, o_a.shape)
+    if tuple(o_a.shape[:-1]) != tuple(lse_a.shape):
+        raise ValueError("o_a and lse_a disagree on the row shape")
+    st = lib().fa_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse), rows,
+                        d, _stream(stream, o_a.device), _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_merge")
+
+
+def fa_fwd_split_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int) -> int:
+    return int(lib().fa_fwd_split_workspace_bytes(B, H, N, d, num_splits))
+
+
+def fa_fwd_split(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=None,
+                 num_splits: int = 2, workspace=None, stream=None) -> None:
+    """Enqueue the key-split forward (same results as fa_fwd). ``workspace``
+    is a device tensor of at least fa_fwd_split_workspace_bytes() bytes, or
+    None to let torch allocate one here (plumbing only)."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("o", o, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    need = fa_fwd_split_workspace_bytes(B, H, N, d, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and not workspace.is_cuda:
+        raise ValueError("workspace must be a device tensor")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                            float(scale), int(bool(causal)), _kv(kv_len, B), int(num_splits),
+                            _ptr(workspace), ws_bytes, _stream(stream, q.device),
+                            _DTYPE.get(q.dtype, -99), _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_split")
 
 
 # Convenience wrappers that allocate the outputs with torch (plumbing only).

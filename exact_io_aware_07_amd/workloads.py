@@ -88,8 +88,14 @@ LONG_BWD = LONG.with_(name="long_context_bf16_bwd", backward=True,
 TRADE_BWD = TRADE.with_(name="trading_day_bf16_causal_bwd", backward=True,
                         measurement_only=True)
 
+# Few heads, long causal sequence: too few query blocks to fill the chip, the
+# shape a key-split forward (the one-GPU half of ring attention) is for.
+FEW_HEADS = Workload("few_heads_long_causal_bf16_split", 1, 2, 32768, 64, "bf16", causal=True,
+                     measurement_only=True,
+                     note="B=1 H=2 N=32768 d=64 bf16 causal, forward plain and key-split")
+
 CONFIGS: Dict[str, Workload] = {w.name: w for w in (TINY, BERT, LONG, TRADE, GPT2)}
-MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD)}
+MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD, FEW_HEADS)}
 ALL: Dict[str, Workload] = {**CONFIGS, **MEASUREMENT}
 
 

@@ -123,6 +123,64 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
               int B, int H, int N, int d, float scale, int causal,
               const int* kv_len, void* stream, int dtype);
 
+/*
+ * Attention over part of the keys, and the merge of such parts: the pieces
+ * of ring attention (Ultralytics glossary page "Flash Attention", section
+ * "Flash Attention e termini correlati": each device keeps its query block
+ * and visits the others' key/value blocks) and of a key-split forward. A
+ * part's result is exact attention over its keys; parts over disjoint key
+ * sets combine exactly by the online-softmax recurrence (marketmaker.cc
+ * article, section "在线softmax递归") applied to whole results:
+ *     m = max_p LSE_p,  w_p = exp(LSE_p - m),
+ *     O = sum_p w_p O_p / sum_p w_p,  LSE = m + ln sum_p w_p.
+ * These entry points take fp16/bf16 inputs only (FA_F32 inputs return
+ * FA_ERR_UNSUPPORTED); partial results are fp32.
+ *
+ * fa_fwd_partial: queries q [B,H,Nq,d] at global positions q_pos0 + i,
+ * keys k, v [B,H,Nk,d] at global positions k_pos0 + j. With causal = 1 a
+ * key is hidden when its position is after the query's (k_pos0 + j >
+ * q_pos0 + i); kv_len (NULL or device int32 [B]) hides local keys
+ * j >= kv_len[b]. Writes o_part fp32 [B,H,Nq,d] (normalised over the part's
+ * visible keys) and lse_part fp32 [B,H,Nq]; a row with no visible key in
+ * the part gets 0 and -inf. Nq, Nk >= 0 (Nk = 0 gives every row 0 / -inf,
+ * and k, v may then be NULL),
+ * |q_pos0|, |k_pos0| < 2^29 (else FA_ERR_INVALID_ARG), Nk * d * 4 < 2^31.
+ * B*H*Nq == 0 returns FA_OK at once.
+ */
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
+                   float* lse_part, int B, int H, int Nq, int Nk, int d,
+                   float scale, int causal, int q_pos0, int k_pos0,
+                   const int* kv_len, void* stream, int in_dtype);
+
+/*
+ * fa_merge: out = merge(a, b) for `rows` rows of d (64 or 128) elements:
+ * o_a, o_b fp32 [rows, d]; lse_a, lse_b fp32 [rows] (-inf marks an empty
+ * part); o [rows, d] in o_dtype (FA_F32, FA_F16 or FA_BF16) and lse fp32
+ * [rows]. With o_dtype = FA_F32, o and lse may be o_a and lse_a (an
+ * accumulator merged in place, as a ring step does); otherwise outputs must
+ * not overlap the inputs. rows == 0 returns FA_OK at once.
+ */
+int fa_merge(const float* o_a, const float* lse_a, const float* o_b,
+             const float* lse_b, void* o, float* lse, long long rows, int d,
+             void* stream, int o_dtype);
+
+/*
+ * Key-split forward: the same O and LSE as fa_fwd (same arguments and
+ * conventions), computed as num_splits (1..16) parts over consecutive key
+ * ranges, one launch for all parts, then one merge launch. Splitting gives
+ * a short, wide problem (few heads, or B = 1) more workgroups to run.
+ * Keys are split in runs of ceil(N / num_splits) rounded up to a multiple
+ * of 64; fewer parts are used when the runs cover N sooner (one part runs
+ * fa_fwd's path and needs no workspace). The workspace holds the parts:
+ * fa_fwd_split_workspace_bytes(B, H, N, d, num_splits) bytes, 16-byte
+ * aligned, owned by the caller, contents on entry ignored.
+ */
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int num_splits);
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal,
+                 const int* kv_len, int num_splits, void* workspace,
+                 size_t workspace_bytes, void* stream, int in_dtype, int o_dtype);
+
 /* Static, human-readable text for a status code. Never NULL. */
 const char* fa_strerror(int status);
 

@@ -148,3 +148,91 @@ def test_stage_entry_points_validate_before_launch():
 def test_sequence_longer_than_a_32_bit_head_is_unsupported():
     assert _fwd(N=4194304, d=128) == fa.FA_ERR_UNSUPPORTED
     assert _fwd(N=8388608, d=64) == fa.FA_ERR_UNSUPPORTED
+
+
+def _part(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0,
+          qp=0, kp=0, kv=None, it=fa.FA_BF16):
+    return fa.lib().fa_fwd_partial(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, qp, kp, kv,
+                                   None, it)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(it=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(qp=1 << 29), fa.FA_ERR_INVALID_ARG),
+    (dict(kp=-(1 << 29)), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=(1 << 31) // 256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_partial_validation(kw, expect):
+    assert _part(**kw) == expect
+
+
+def test_empty_partial_is_ok_without_pointers():
+    assert _part(q=None, k=None, v=None, o=None, lse=None, Nq=0) == fa.FA_OK
+
+
+def _merge(oa=A, la=A, ob=A, lb=A, o=A, lse=A, rows=16, d=64, ot=fa.FA_F32):
+    return fa.lib().fa_merge(oa, la, ob, lb, o, lse, rows, d, None, ot)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(ot=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(rows=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(ob=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(lb=A + 1), fa.FA_ERR_INVALID_ARG),
+])
+def test_merge_validation(kw, expect):
+    assert _merge(**kw) == expect
+
+
+def test_empty_merge_is_ok_without_pointers():
+    assert _merge(oa=None, la=None, ob=None, lb=None, o=None, lse=None, rows=0) == fa.FA_OK
+
+
+def _split(ws=A, ws_bytes=1 << 30, B=1, H=1, N=1000, d=64, splits=4, it=fa.FA_BF16,
+           ot=fa.FA_BF16, o=A):
+    return fa.lib().fa_fwd_split(A, A, A, o, A, B, H, N, d, 0.125, 0, None, splits, ws,
+                                 ws_bytes, None, it, ot)
+
+
+def test_split_workspace_counts_every_part():
+    # N = 1000 in 4 parts: runs of ceil(1000 / 4) = 250 keys, rounded up to
+    # 256, need 4 parts; each part keeps d + 1 fp32 per query row
+    assert fa.fa_fwd_split_workspace_bytes(2, 3, 1000, 64, 4) == 4 * 2 * 3 * 1000 * 65 * 4
+    # N = 100 in 4 parts: runs of 64 keys cover it in 2 parts
+    assert fa.fa_fwd_split_workspace_bytes(1, 1, 100, 128, 4) == 2 * 100 * 129 * 4
+    # one part (or N <= 64) runs the plain forward and needs none
+    assert fa.fa_fwd_split_workspace_bytes(1, 1, 1000, 64, 1) == 0
+    assert fa.fa_fwd_split_workspace_bytes(1, 1, 64, 64, 8) == 0
+    assert fa.fa_fwd_split_workspace_bytes(1, 1, 1000, 64, 0) == 0
+    assert fa.fa_fwd_split_workspace_bytes(1, 1, 1000, 64, 17) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=17), fa.FA_ERR_INVALID_ARG),
+    (dict(it=fa.FA_F32, ot=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(ot=fa.FA_F16), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 8), fa.FA_ERR_WORKSPACE),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+])
+def test_split_validation(kw, expect):
+    assert _split(**kw) == expect
+
+
+def test_partial_without_keys_needs_no_key_pointers():
+    # validation only: a null k / v is accepted when Nk == 0 and rejected otherwise
+    assert _part(k=None, v=None, Nk=5) == fa.FA_ERR_INVALID_ARG
+    assert _part(k=A + 8, Nk=5) == fa.FA_ERR_INVALID_ARG
