@@ -9,3 +9,4 @@ from .attention import attn_bwd64, attn_bwd64_sampled, attn_fwd64, attn_probs64,
 from .brute import brute_head_forward, brute_head_grad_fd, brute_head_part, brute_loss  # noqa: F401
 from .memory import score_matrix_bytes  # noqa: F401
 from .split import attn_part64, merge64  # noqa: F401
+from .gqa import attn_bwd64_gqa, attn_fwd64_gqa  # noqa: F401
