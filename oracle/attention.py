@@ -15,7 +15,7 @@ oracle. The definition is the one given in the marketmaker.cc article,
 sections "为什么注意力是受记忆限制的" (why attention is memory-bound) and
 "集成是八行" (the three-line materialised path it replaces).
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
   * causal means key j is hidden from query i when j > i, top-left aligned
     (marketmaker.cc article, section "因果掩盖..." / causal masking: tiles whose
     keys lie wholly in the future of their queries are skipped);

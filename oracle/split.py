@@ -14,7 +14,7 @@ row's LSE stands for its pair (m, l):
     m = max(LSE_a, LSE_b),   w_a = exp(LSE_a - m),   w_b = exp(LSE_b - m),
     O = (w_a O_a + w_b O_b) / (w_a + w_b),   LSE = m + ln(w_a + w_b).
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
   * a partial step attends queries at global positions q_pos0 + i to keys
     at global positions k_pos0 + j; causal hides a key whose position is
     after the query's; key padding hides local keys j >= kv_len[b];
