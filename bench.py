@@ -53,10 +53,11 @@ def fwd_flops(w) -> float:
 def compulsory_bytes(w, backward: bool) -> float:
     """Bytes the pass must move to or from HBM at least: forward reads Q, K, V
     and writes O and LSE; backward reads Q, K, V, O, dO, LSE (and D) and
-    writes dQ, dK, dV (and D)."""
+    writes dQ, dK, dV (and D). K, V, dK, dV have the workload's K/V heads."""
     e = 4 if w.dtype == "fp32" else 2
-    per_row = (8 * w.d * e + 8) if backward else (4 * w.d * e + 4)
-    return float(w.B * w.H * w.N * per_row)
+    q_row = (4 * w.d * e + 8) if backward else (2 * w.d * e + 4)   # per query row
+    kv_row = (4 * w.d * e) if backward else (2 * w.d * e)          # per key row of a K/V head
+    return float(w.B * w.N * (w.H * q_row + w.kv_heads * kv_row))
 
 
 def device_info(torch) -> dict:
@@ -234,7 +235,65 @@ def run_gpu(args):
     if not args.no_extra:
         out["extra"] = extra_configs(torch, W)
         out["extra"][W.FEW_HEADS.name] = split_config(torch, W)
+        out["extra"][W.GQA.name] = gqa_config(torch, W)
     return out
+
+
+def median_ms(torch, fn, iters: int = 10) -> float:
+    """Median per-call time of ``fn`` in batches of ``iters`` calls between two
+    events, after 0.3 s of warm-up, over at least 50 calls and 100 ms."""
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 0.3:
+        fn()
+        torch.cuda.synchronize()
+    batches = []
+    while len(batches) * iters < 50 or sum(batches) * iters < 100.0:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        batches.append(s.elapsed_time(e) / iters)
+    return statistics.median(batches)
+
+
+def gqa_config(torch, W):
+    """Grouped-query attention (32 query heads on 8 K/V heads): forward and
+    backward through fa_fwd_gqa / fa_bwd_gqa, and for comparison the plain
+    entry points on K/V repeated over each group (the same FLOPs, four times
+    the K/V bytes)."""
+    from exact_io_aware_07_amd import fa_bwd, fa_bwd_gqa, fa_bwd_gqa_workspace_bytes, fa_fwd, fa_fwd_gqa
+    w = W.GQA
+    inp = W.make_inputs(w)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    G = w.H // w.kv_heads
+    kr, vr = (t.repeat_interleave(G, dim=1).contiguous() for t in (k, v))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    dk, dv, dkr, dvr = (torch.empty_like(t) for t in (k, v, kr, vr))
+    ws_bytes = max(fa_bwd_gqa_workspace_bytes(w.B, w.H, w.kv_heads, w.N, w.d), w.B * w.H * w.N * 4)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    fa_fwd_gqa(q, k, v, o, lse, w.scale, w.causal)
+    runs = {
+        "fwd_gqa": (lambda: fa_fwd_gqa(q, k, v, o, lse, w.scale, w.causal), 1.0),
+        "bwd_gqa": (lambda: fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal,
+                                       None, ws), 2.5),
+        "fwd_repeated_kv": (lambda: fa_fwd(q, kr, vr, o, lse, w.scale, w.causal), 1.0),
+        "bwd_repeated_kv": (lambda: fa_bwd(q, kr, vr, o, do, lse, dq, dkr, dvr, w.scale, w.causal,
+                                           None, ws), 2.5),
+    }
+    entry = {"H": w.H, "Hkv": w.kv_heads, "B": w.B, "N": w.N, "d": w.d,
+             "gqa_workspace_bytes": fa_bwd_gqa_workspace_bytes(w.B, w.H, w.kv_heads, w.N, w.d)}
+    for name, (fn, mult) in runs.items():
+        ms = median_ms(torch, fn)
+        rate = mult * fwd_flops(w) / (ms * 1e-3)
+        entry[f"{name}_ms"] = ms
+        entry[f"{name}_tflops"] = rate / 1e12
+        entry[f"{name}_pct_of_bf16_peak"] = 100 * rate / PEAK_BF16_FLOPS
+    log(f"[bench] extra {w.name}: {entry}")
+    return entry
 
 
 def extra_configs(torch, W, iters: int = 10):

@@ -40,8 +40,9 @@ fa::Elem elem(int t) {
 int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, float* dsum, const int* kv_len,
                int B, int H, int N, int d, float scale, int causal, void* stream, int dtype,
-               int stages) {
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dsum, kv_len, B, H, N, d, scale, causal};
+               int stages, int Hkv = 0, int gsplit = 1, float* dkv_part = nullptr) {
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dsum, kv_len, B, H, N, d, scale, causal,
+                Hkv > 0 ? Hkv : H, gsplit, dkv_part};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = (dtype == FA_F32) ? fa::launch_bwd_f32(a, stages, s)
                                    : fa::launch_bwd_mfma(a, elem(dtype), stages, s);
@@ -61,6 +62,17 @@ void split_plan(int N, int num_splits, int* ksplit, int* parts) {
 size_t split_workspace(int B, int H, int N, int d, int parts) {
   if (parts <= 1) return 0;
   return (size_t)parts * (size_t)B * H * N * (size_t)(d + 1) * sizeof(float);
+}
+
+// Workspace of the grouped backward: D for every query row, then (when the
+// dK/dV stage splits each group's query heads) the fp32 partial dK and dV.
+size_t dsum_bytes_aligned(int B, int H, int N) {
+  return (((size_t)B * H * N * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+size_t gqa_part_bytes(int B, int Hkv, int N, int d, int gsplit) {
+  if (gsplit <= 1) return 0;
+  return 2 * (size_t)gsplit * B * Hkv * N * (size_t)d * sizeof(float);
 }
 
 // Positions of a partial step are bounded so that every sum of a position
@@ -84,7 +96,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return FA_ERR_INVALID_ARG;
   if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
 
-  fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0};
+  fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0, H};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = (in_dtype == FA_F32) ? fa::launch_fwd_f32(a, s)
                                       : fa::launch_fwd_mfma(a, elem(in_dtype), elem(o_dtype), s);
@@ -180,7 +192,7 @@ int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, f
   if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
 
   fa::FwdArgs a{q, k, v, o_part, lse_part, kv_len, B, H, Nq, d, scale, causal,
-                Nk, q_pos0, k_pos0, 1, Nk, 0, 0};
+                Nk, q_pos0, k_pos0, 1, Nk, 0, 0, H};
   hipError_t e = fa::launch_fwd_mfma_general(a, elem(in_dtype), (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -234,7 +246,7 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
   split_plan(N, num_splits, &ks, &parts);
   hipStream_t s = (hipStream_t)stream;
   if (parts == 1) {
-    fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0};
+    fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0, H};
     hipError_t e = fa::launch_fwd_mfma(a, elem(in_dtype), elem(o_dtype), s);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
@@ -244,7 +256,7 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
   const long long so = (long long)B * H * N * d;
   const long long sl = (long long)B * H * N;
   float* wl = wo + parts * so;
-  fa::FwdArgs a{q, k, v, wo, wl, kv_len, B, H, N, d, scale, causal, N, 0, 0, parts, ks, so, sl};
+  fa::FwdArgs a{q, k, v, wo, wl, kv_len, B, H, N, d, scale, causal, N, 0, 0, parts, ks, so, sl, H};
   hipError_t e = fa::launch_fwd_mfma_general(a, elem(in_dtype), s);
   if (e != hipSuccess) return FA_ERR_HIP;
   fa::MergeArgs m{};
@@ -260,12 +272,61 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Hkv, int N, int d, float scale, int causal, const int* kv_len, void* stream,
+               int in_dtype, int o_dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0, Hkv};
+  hipError_t e = fa::launch_fwd_mfma(a, elem(in_dtype), elem(o_dtype), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+  if (B < 0 || H < 0 || N < 0 || Hkv < 1 || H % Hkv != 0 || (d != 64 && d != 128)) return 0;
+  if (H == 0) return 0;
+  return dsum_bytes_aligned(B, H, N) +
+         gqa_part_bytes(B, Hkv, N, d, fa::bwd_group_split(B, H, Hkv, N, d));
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+               float scale, int causal, const int* kv_len, void* workspace,
+               size_t workspace_bytes, void* stream, int dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < fa_bwd_gqa_workspace_bytes(B, H, Hkv, N, d))
+    return FA_ERR_WORKSPACE;
+  const int gsplit = fa::bwd_group_split(B, H, Hkv, N, d);
+  float* part = gsplit > 1 ? (float*)((char*)workspace + dsum_bytes_aligned(B, H, N)) : nullptr;
+  return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d,
+                    scale, causal, stream, dtype,
+                    (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV, Hkv, gsplit, part);
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success (work enqueued)";
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: null or misaligned pointer, negative size, bad scale or flag";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128; dtype pair not supported";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or smaller than the entry point's *_workspace_bytes()";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
     default: return "unknown fa status";
   }

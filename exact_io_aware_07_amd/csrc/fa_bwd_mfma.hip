@@ -116,20 +116,35 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 
   const int N = a.N;
   const int nkb = (N + BK - 1) / BK;
-  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nkb, a.B * a.H, a.causal, DkdvCfg<D>::MINW);
-  const int bh = pk.bh;
+  // One workgroup per (b, K/V head, query-head share, key block); with
+  // grouped K/V heads it runs the tiles of each query head of its share in
+  // turn (a share is G / gsplit consecutive heads of the group of G).
+  const int S = a.gsplit;
+  const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nkb, a.B * a.Hkv * S, a.causal,
+                                  DkdvCfg<D>::MINW);
+  const int bhk = pk.bh / S;  // K/V head
+  const int share = pk.bh - bhk * S;
   const int kb = pk.rank;  // causal: key block 0 sees every query and has the most work
-  const int b = bh / a.H;
+  const int b = bhk / a.Hkv;
+  const int G = a.H / a.Hkv;
+  const int g0 = share * (G / S), g1 = g0 + G / S;
 
-  const size_t head_off = (size_t)bh * N * D;
-  const float* __restrict__ Lg = a.lse + (size_t)bh * N;
-  const float* __restrict__ Dg = a.dsum + (size_t)bh * N;
+  const size_t head_off = (size_t)bhk * N * D;  // K, V, dK, dV
   int kv_end = N;
   if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + head_off, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint16_t*)a.dout + head_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + head_off, (uint32_t)kv_end * D * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + head_off, (uint32_t)kv_end * D * 2);
+  // Q, dO, LSE and D of the query head being run (set per query head below)
+  __amdgpu_buffer_rsrc_t rq, rg;
+  const float* __restrict__ Lg;
+  const float* __restrict__ Dg;
+  auto set_query_head = [&](int g) {
+    const size_t bhq = (size_t)b * a.H + (size_t)(bhk - b * a.Hkv) * G + g;
+    rq = make_rsrc((const uint16_t*)a.q + bhq * N * D, (uint32_t)N * D * 2);
+    rg = make_rsrc((const uint16_t*)a.dout + bhq * N * D, (uint32_t)N * D * 2);
+    Lg = a.lse + bhq * N;
+    Dg = a.dsum + bhq * N;
+  };
 
   const int key0 = kb * BK + wave * 32;
   const int my_key = key0 + kl;
@@ -188,16 +203,18 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
     load_tile_lds<D, BQ, kBwdWaves>(rg, gbuf(p), it * BQ, wave, lane);
   };
 
-  if (qt_begin < qt_end) {
-    load_tiles(qt_begin, qt_begin & 1);
-    load_stats(qt_begin);
-    store_stats(qt_begin & 1);
-  }
-  // Unconditional, so that on every path into the loops below the K and V
-  // fragment loads above are known complete: the compiler places waits path
-  // by path, and would otherwise wait for them inside every tile, which at
-  // run time also waits for that tile's own prefetch copies.
-  __builtin_amdgcn_s_waitcnt(0);
+  auto prologue = [&]() {
+    if (qt_begin < qt_end) {
+      load_tiles(qt_begin, qt_begin & 1);
+      load_stats(qt_begin);
+      store_stats(qt_begin & 1);
+    }
+    // Unconditional, so that on every path into the loops below the K and
+    // V fragment loads above are known complete: the compiler places waits
+    // path by path, and would otherwise wait for them inside every tile,
+    // which at run time also waits for that tile's own prefetch copies.
+    __builtin_amdgcn_s_waitcnt(0);
+  };
 
   // One query tile. FULL tiles (every key of the workgroup visible to every
   // query of the tile) run with no liveness test and no mask, so both query
@@ -277,18 +294,44 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   int it_full = qt_end;
   if (blk_key0 + BK <= kv_end) it_full = a.causal ? max(qt_begin, (blk_key0 + BK - 1 + BQ - 1) / BQ) : qt_begin;
   it_full = min(it_full, qt_end);
-  int it = qt_begin;
-  for (; it < it_full; ++it) tile(it, Part{}, it & 1);
-  // Full tiles in pairs of known parity (an odd first tile on its own).
-  if (it < qt_end && (it & 1)) tile(it++, Full{}, 1);
-  for (; it + 1 < qt_end; it += 2) {
-    tile(it, Full{}, 0);
-    tile(it + 1, Full{}, 1);
+  for (int g = g0; g < g1; ++g) {
+    set_query_head(g);
+    // Every wave is done with the previous query head's last tile before
+    // this head's first tile is copied into the buffers.
+    if (g > g0) __syncthreads();
+    prologue();
+    int it = qt_begin;
+    for (; it < it_full; ++it) tile(it, Part{}, it & 1);
+    // Full tiles in pairs of known parity (an odd first tile on its own).
+    if (it < qt_end && (it & 1)) tile(it++, Full{}, 1);
+    for (; it + 1 < qt_end; it += 2) {
+      tile(it, Full{}, 0);
+      tile(it + 1, Full{}, 1);
+    }
+    if (it < qt_end) tile(it, Full{}, 0);
   }
-  if (it < qt_end) tile(it, Full{}, 0);
 
   // dK^T / dV^T accumulators: lane = key, registers = d in runs of 4.
-  if (my_key < N) {
+  if (S > 1) {
+    // fp32 partials of this share; the reduction adds the shares in order.
+    if (my_key < N) {
+      const size_t part = (size_t)a.B * a.Hkv * N * D;
+      float* dKp = a.dkv_part + share * part + head_off + (size_t)my_key * D;
+      float* dVp = dKp + (size_t)S * part;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = dt * 32 + r4 * 8 + 4 * hh;
+          const f32x16& K4 = dk[dt];
+          const f32x16& V4 = dv[dt];
+          *(f32x4*)(dKp + d0) = f32x4{K4[4 * r4] * a.scale, K4[4 * r4 + 1] * a.scale,
+                                      K4[4 * r4 + 2] * a.scale, K4[4 * r4 + 3] * a.scale};
+          *(f32x4*)(dVp + d0) = f32x4{V4[4 * r4], V4[4 * r4 + 1], V4[4 * r4 + 2], V4[4 * r4 + 3]};
+        }
+      }
+    }
+  } else if (my_key < N) {
     uint16_t* dKg = (uint16_t*)a.dk + head_off + (size_t)my_key * D;
     uint16_t* dVg = (uint16_t*)a.dv + head_off + (size_t)my_key * D;
 #pragma unroll
@@ -362,8 +405,10 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), N);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + head_off, (uint32_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc((const uint16_t*)a.dout + head_off, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + head_off, (uint32_t)kv_end * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + head_off, (uint32_t)kv_end * D * 2);
+  // K/V head of this query head (grouped K/V heads share one among H / Hkv)
+  const size_t kv_off = (size_t)(b * a.Hkv + (bh - b * a.H) / (a.H / a.Hkv)) * N * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint16_t*)a.k + kv_off, (uint32_t)kv_end * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint16_t*)a.v + kv_off, (uint32_t)kv_end * D * 2);
 
   const int q_blk0 = qb * BR;
   int kv_lim = kv_end;
@@ -518,6 +563,32 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   }
 }
 
+// dK, dV = the sum of the S fp32 partials of the grouped dK/dV stage, in
+// share order, rounded once to the storage type. HBM-bound: per element
+// 4 * S bytes read, 2 written. n4 = elements per tensor / 4.
+template <typename T>
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* __restrict__ part,
+                                                         uint16_t* __restrict__ dk,
+                                                         uint16_t* __restrict__ dv, long long n4,
+                                                         int S) {
+  const long long step = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * n4; i += step) {
+    const int t = i >= n4;  // 0: dK, 1: dV
+    const long long j = i - t * n4;
+    const f32x4* p = (const f32x4*)part + (long long)t * S * n4 + j;
+    f32x4 acc = p[0];
+    for (int sh = 1; sh < S; ++sh) {
+      const f32x4 x = p[sh * n4];
+      acc[0] += x[0];
+      acc[1] += x[1];
+      acc[2] += x[2];
+      acc[3] += x[3];
+    }
+    uint16_t* out = (t ? dv : dk) + 4 * j;
+    *(u32x2*)out = u32x2{Mfma<T>::pack(acc[0], acc[1]), Mfma<T>::pack(acc[2], acc[3])};
+  }
+}
+
 template <typename T, int D>
 hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   hipError_t e = hipSuccess;
@@ -536,9 +607,17 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   }
   if (stages & (int)BwdStage::DKDV) {
     const long nkb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nkb)),
-                       dim3(kBwdThreads), 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<T, D>),
+                       dim3((unsigned)((long)a.B * a.Hkv * a.gsplit * nkb)), dim3(kBwdThreads),
+                       0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.gsplit > 1) {
+      const long long n4 = (long long)a.B * a.Hkv * a.N * D / 4;
+      const long long blocks = (2 * n4 + 255) / 256 < 8192 ? (2 * n4 + 255) / 256 : 8192;
+      hipLaunchKernelGGL((dkv_reduce_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         a.dkv_part, (uint16_t*)a.dk, (uint16_t*)a.dv, n4, a.gsplit);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   return e;
 }
@@ -549,6 +628,16 @@ hipError_t launch_t(const BwdArgs& a, int stages, hipStream_t st) {
 }
 
 }  // namespace
+
+int bwd_group_split(int B, int H, int Hkv, int N, int d) {
+  const int G = H / Hkv;
+  const long long nkb = (N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+  const long long slots = 8LL * kCusPerXcd * (d == 128 ? DkdvCfg<128>::MINW : DkdvCfg<64>::MINW);
+  const long long base = (long long)B * Hkv * nkb;
+  for (int s = 1; s < G; ++s)
+    if (G % s == 0 && base * s >= 2 * slots) return s;
+  return G;
+}
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, Elem t, int stages, hipStream_t st) {
   return (t == Elem::BF16) ? launch_t<BF16>(a, stages, st) : launch_t<F16>(a, stages, st);

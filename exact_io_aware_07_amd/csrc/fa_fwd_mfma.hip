@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
 
   const size_t head_off = (size_t)bh * N * D;          // Q and O
   const int Nk = GEN ? a.Nk : N;
-  const size_t head_k = (size_t)bh * Nk * D;           // K and V
+  const int kvh = b * a.Hkv + (bh - b * a.H) / (a.H / a.Hkv);  // K/V head of this query head
+  const size_t head_k = (size_t)kvh * Nk * D;          // K and V
   const int k_lo = GEN ? split * a.ksplit : 0;         // this split's keys: [k_lo, k_hi)
   int kv_end = GEN ? min(k_lo + a.ksplit, Nk) : N;     // keys visible at all (exclusive)
   if (a.kv_len) kv_end = min(max(a.kv_len[b], 0), kv_end);

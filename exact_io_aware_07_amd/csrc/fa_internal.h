@@ -28,6 +28,9 @@ struct FwdArgs {
   int q_pos0, k_pos0;
   int nsplit, ksplit;  // split s streams keys [s * ksplit, (s + 1) * ksplit)
   long long o_split_stride, lse_split_stride;  // elements between splits' outputs
+  // K/V heads (H for plain attention): query head h of a batch uses K/V head
+  // h / (H / Hkv); K and V are [B, Hkv, Nk, d].
+  int Hkv;
 };
 
 struct BwdArgs {
@@ -45,7 +48,21 @@ struct BwdArgs {
   int B, H, N, d;
   float scale;
   int causal;
+  // K/V heads, as in FwdArgs: K, V, dK, dV are [B, Hkv, N, d]; a K/V head's
+  // gradient sums over its H / Hkv query heads.
+  int Hkv;
+  // gsplit > 1: each K/V head's query heads are shared among gsplit
+  // workgroups per key block, which write fp32 partial dK, dV to dkv_part
+  // ([2][gsplit][B, Hkv, N, d]: every dK part, then every dV part); a
+  // reduction then sums the parts into dk, dv. gsplit divides H / Hkv.
+  int gsplit;
+  float* dkv_part;
 };
+
+// Query-head split of the grouped dK/dV stage for a shape: the smallest
+// divisor of H / Hkv that gives the stage at least two workgroups per
+// resident slot of the chip (1 when the K/V heads alone do that).
+int bwd_group_split(int B, int H, int Hkv, int N, int d);
 
 // Launchers return hipSuccess or the launch error. Arguments are validated
 // by the caller.

@@ -20,7 +20,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0,
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_dsum", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_partial", "fa_merge", "fa_fwd_split_workspace_bytes",
-           "fa_fwd_split", "fa_strerror")
+           "fa_fwd_split", "fa_fwd_gqa", "fa_bwd_gqa_workspace_bytes", "fa_bwd_gqa",
+           "fa_strerror")
 
 _DTYPE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib: Optional[ctypes.CDLL] = None
@@ -61,6 +62,13 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_split_workspace_bytes.restype = sz
     L.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, sz, vp, i, i]
     L.fa_fwd_split.restype = i
+    L.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, i, i]
+    L.fa_fwd_gqa.restype = i
+    L.fa_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_bwd_gqa_workspace_bytes.restype = sz
+    L.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz,
+                             vp, i]
+    L.fa_bwd_gqa.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -260,7 +268,62 @@ def fa_fwd_split(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=Non
         raise FaError(st, "fa_fwd_split")
 
 
+def _gqa_shapes(q, k):
+    B, H, N, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, Hkv, {N}, {d}]")
+    return B, H, int(k.shape[1]), N, d
+
+
+def fa_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=None,
+               stream=None) -> None:
+    """Enqueue grouped-query attention: q, o [B, H, N, d]; k, v [B, Hkv, N, d]
+    with H % Hkv == 0 (query head h uses K/V head h // (H // Hkv)); lse fp32
+    [B, H, N]."""
+    B, H, Hkv, N, d = _gqa_shapes(q, k)
+    _check_tensor("q", q, q.shape)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, Hkv, N, d), q.dtype)
+    _check_tensor("o", o, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    st = lib().fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                          float(scale), int(bool(causal)), _kv(kv_len, B),
+                          _stream(stream, q.device), _DTYPE.get(q.dtype, -99),
+                          _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_gqa")
+
+
+def fa_bwd_gqa_workspace_bytes(B: int, H: int, Hkv: int, N: int, d: int) -> int:
+    return int(lib().fa_bwd_gqa_workspace_bytes(B, H, Hkv, N, d))
+
+
+def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False,
+               kv_len=None, workspace=None, stream=None) -> None:
+    """Enqueue the grouped-query backward: dq [B, H, N, d]; dk, dv
+    [B, Hkv, N, d], each the sum over the K/V head's query heads."""
+    B, H, Hkv, N, d = _gqa_shapes(q, k)
+    for name, t in (("o", o), ("dout", dout), ("dq", dq)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, (B, Hkv, N, d), q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    need = fa_bwd_gqa_workspace_bytes(B, H, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                          _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale), int(bool(causal)),
+                          _kv(kv_len, B), _ptr(workspace), ws_bytes, _stream(stream, q.device),
+                          _DTYPE.get(q.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_gqa")
+
+
 # Convenience wrappers that allocate the outputs with torch (plumbing only).
+
+# K and V with fewer heads than Q go to the grouped-query entry points.
 
 def attention_forward(q, k, v, causal: bool = False, kv_len=None, scale: Optional[float] = None,
                       out_dtype: Optional[torch.dtype] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -268,7 +331,10 @@ def attention_forward(q, k, v, causal: bool = False, kv_len=None, scale: Optiona
     scale = d ** -0.5 if scale is None else scale
     o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, scale, causal, kv_len, stream)
+    if k.dim() == 4 and k.shape[1] != H:
+        fa_fwd_gqa(q, k, v, o, lse, scale, causal, kv_len, stream)
+    else:
+        fa_fwd(q, k, v, o, lse, scale, causal, kv_len, stream)
     return o, lse
 
 
@@ -276,6 +342,9 @@ def attention_backward(q, k, v, o, dout, lse, causal: bool = False, kv_len=None,
                        scale: Optional[float] = None, stream=None):
     d = q.shape[-1]
     scale = d ** -0.5 if scale is None else scale
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len, None, stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if k.dim() == 4 and k.shape[1] != q.shape[1]:
+        fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len, None, stream)
+    else:
+        fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len, None, stream)
     return dq, dk, dv

@@ -7,7 +7,8 @@ from it without sharing any computation.
 Recipe (applies to every workload):
   * one ``torch.Generator`` on the CPU, seeded (default seed 0);
   * fp32 standard-normal draws in the order Q, K, V, then dO (only for
-    workloads with a backward pass), each of shape [B, H, N, d];
+    workloads with a backward pass), each of shape [B, H, N, d] (K and V
+    [B, Hkv, N, d] for a workload with grouped K/V heads);
   * then the per-workload extras, in this order: the key-padding lengths
     (``randint(lo, hi + 1, (B,))``), then the outlier key rows (for each
     (b, h) in row-major order, ``randperm(N)[:round(frac * N)]`` and those K
@@ -48,7 +49,12 @@ class Workload:
     k_outlier_scale: float = 1.0
     backward: bool = False
     measurement_only: bool = False
+    Hkv: Optional[int] = None  # K/V heads (grouped-query attention); None means H
     note: str = field(default="", compare=False)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
     @property
     def scale(self) -> float:
@@ -94,23 +100,32 @@ FEW_HEADS = Workload("few_heads_long_causal_bf16_split", 1, 2, 32768, 64, "bf16"
                      measurement_only=True,
                      note="B=1 H=2 N=32768 d=64 bf16 causal, forward plain and key-split")
 
+# Grouped-query attention: the 32 query heads and 4096 tokens of the
+# long-context shape sharing 8 K/V heads (groups of 4), causal, forward and
+# backward, two sequences.
+GQA = Workload("long_context_gqa_bf16_causal_fwd_bwd", 2, 32, 4096, 128, "bf16", causal=True,
+               backward=True, measurement_only=True, Hkv=8,
+               note="B=2 H=32 Hkv=8 N=4096 d=128 bf16 causal, forward + backward")
+
 CONFIGS: Dict[str, Workload] = {w.name: w for w in (TINY, BERT, LONG, TRADE, GPT2)}
-MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD, FEW_HEADS)}
+MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD, FEW_HEADS, GQA)}
 ALL: Dict[str, Workload] = {**CONFIGS, **MEASUREMENT}
 
 
 def make_inputs(w: Workload, seed: int = 0) -> Dict[str, Optional[torch.Tensor]]:
     """Draw the seeded inputs of ``w`` on the CPU, already cast to its dtype.
 
-    Returns a dict with ``q, k, v`` (and ``do`` when ``w.backward``) as
-    contiguous [B, H, N, d] tensors and ``kv_len`` as an int32 [B] tensor or
+    Returns a dict with ``q`` (and ``do`` when ``w.backward``) as contiguous
+    [B, H, N, d] tensors, ``k, v`` as [B, Hkv, N, d] (Hkv = H unless the
+    workload groups its K/V heads) and ``kv_len`` as an int32 [B] tensor or
     ``None``. The same seed always yields bit-identical tensors.
     """
     g = torch.Generator(device="cpu").manual_seed(seed)
     shape = (w.B, w.H, w.N, w.d)
+    kv_shape = (w.B, w.kv_heads, w.N, w.d)
     q = torch.randn(shape, generator=g, dtype=torch.float32)
-    k = torch.randn(shape, generator=g, dtype=torch.float32)
-    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(kv_shape, generator=g, dtype=torch.float32)
+    v = torch.randn(kv_shape, generator=g, dtype=torch.float32)
     do = torch.randn(shape, generator=g, dtype=torch.float32) if w.backward else None
     kv_len = None
     if w.kv_len_range is not None:
@@ -120,7 +135,7 @@ def make_inputs(w: Workload, seed: int = 0) -> Dict[str, Optional[torch.Tensor]]
     if w.k_outlier_frac > 0.0:
         count = int(round(w.k_outlier_frac * w.N))
         for b in range(w.B):
-            for h in range(w.H):
+            for h in range(w.kv_heads):
                 idx = torch.randperm(w.N, generator=g)[:count]
                 k[b, h, idx] *= w.k_outlier_scale
     dt = w.torch_dtype
@@ -135,30 +150,32 @@ def make_inputs(w: Workload, seed: int = 0) -> Dict[str, Optional[torch.Tensor]]
 
 
 def outlier_rows(w: Workload, seed: int = 0) -> Optional[torch.Tensor]:
-    """The [B, H, count] indices of the scaled K rows drawn by ``make_inputs``."""
+    """The [B, Hkv, count] indices of the scaled K rows drawn by ``make_inputs``."""
     if w.k_outlier_frac <= 0.0:
         return None
     g = torch.Generator(device="cpu").manual_seed(seed)
     shape = (w.B, w.H, w.N, w.d)
-    for _ in range(4 if w.backward else 3):
-        torch.randn(shape, generator=g, dtype=torch.float32)
+    kv_shape = (w.B, w.kv_heads, w.N, w.d)
+    for s in (shape, kv_shape, kv_shape) + ((shape,) if w.backward else ()):
+        torch.randn(s, generator=g, dtype=torch.float32)
     if w.kv_len_range is not None:
         lo, hi = w.kv_len_range
         torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64)
     count = int(round(w.k_outlier_frac * w.N))
-    rows = torch.empty((w.B, w.H, count), dtype=torch.int64)
+    rows = torch.empty((w.B, w.kv_heads, count), dtype=torch.int64)
     for b in range(w.B):
-        for h in range(w.H):
+        for h in range(w.kv_heads):
             rows[b, h] = torch.randperm(w.N, generator=g)[:count]
     return rows
 
 
 def random_case(B: int, H: int, N: int, d: int, dtype: str, seed: int,
                 causal: bool = False, kv_len: Optional[list] = None,
-                backward: bool = False) -> Dict[str, Optional[torch.Tensor]]:
+                backward: bool = False, Hkv: Optional[int] = None
+                ) -> Dict[str, Optional[torch.Tensor]]:
     """Seeded inputs for an ad-hoc shape (tails, edge cases), same recipe."""
     w = Workload(f"case_{B}x{H}x{N}x{d}_{dtype}", B, H, N, d, dtype,
-                 causal=causal, backward=backward)
+                 causal=causal, backward=backward, Hkv=Hkv)
     out = make_inputs(w, seed)
     if kv_len is not None:
         out["kv_len"] = torch.tensor(kv_len, dtype=torch.int32)

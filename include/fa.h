@@ -181,6 +181,34 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
                  const int* kv_len, int num_splits, void* workspace,
                  size_t workspace_bytes, void* stream, int in_dtype, int o_dtype);
 
+/*
+ * Grouped-query attention: H query heads share Hkv key/value heads, query
+ * head h of a batch using K/V head h / (H / Hkv). The tiled computation is
+ * unchanged by how many K/V heads there are (delect.ru glossary page
+ * "FlashAttention", section "Что подтверждено"); each query head's result
+ * is plain attention against its K/V head, so Hkv == H is fa_fwd / fa_bwd.
+ *   q, o, dout, dq  [B,H,N,d];  k, v, dk, dv  [B,Hkv,N,d];  lse [B,H,N].
+ *   Hkv >= 1 and H % Hkv == 0, else FA_ERR_INVALID_ARG.
+ * dK and dV of a K/V head are the sums over its H / Hkv query heads, in
+ * fp32, rounded once to dtype. When B * Hkv is too small to fill the chip,
+ * a group's query heads are shared among several workgroups that write
+ * fp32 partial sums to the workspace, added in a fixed order by a second
+ * launch; the result is deterministic either way. The workspace of
+ * fa_bwd_gqa is fa_bwd_gqa_workspace_bytes(B, H, Hkv, N, d) bytes (0 for
+ * invalid sizes), 16-byte aligned, owned by the caller, contents on entry
+ * ignored. Everything else is as for fa_fwd / fa_bwd. fp16/bf16 only
+ * (FA_F32 returns FA_ERR_UNSUPPORTED).
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, float scale, int causal,
+               const int* kv_len, void* stream, int in_dtype, int o_dtype);
+size_t fa_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+               int B, int H, int Hkv, int N, int d, float scale, int causal,
+               const int* kv_len, void* workspace, size_t workspace_bytes,
+               void* stream, int dtype);
+
 /* Static, human-readable text for a status code. Never NULL. */
 const char* fa_strerror(int status);
 

@@ -236,3 +236,71 @@ def test_partial_without_keys_needs_no_key_pointers():
     # validation only: a null k / v is accepted when Nk == 0 and rejected otherwise
     assert _part(k=None, v=None, Nk=5) == fa.FA_ERR_INVALID_ARG
     assert _part(k=A + 8, Nk=5) == fa.FA_ERR_INVALID_ARG
+
+
+def _fwd_gqa(q=A, k=A, v=A, o=A, lse=A, B=1, H=4, Hkv=2, N=16, d=64, scale=0.125, causal=0,
+             kv=None, it=fa.FA_BF16, ot=fa.FA_BF16):
+    return fa.lib().fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, kv, None, it, ot)
+
+
+def _bwd_gqa(ws=A, ws_bytes=1 << 20, B=1, H=4, Hkv=2, N=16, d=64, scale=0.125, causal=0,
+             dtype=fa.FA_BF16, dk=A):
+    return fa.lib().fa_bwd_gqa(A, A, A, A, A, A, A, dk, A, B, H, Hkv, N, d, scale, causal, None,
+                               ws, ws_bytes, None, dtype)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),           # 4 query heads do not split into 3 groups
+    (dict(H=4, Hkv=8), fa.FA_ERR_INVALID_ARG),      # more K/V heads than query heads
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(v=A + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(it=fa.FA_F32, ot=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(it=fa.FA_BF16, ot=fa.FA_F16), fa.FA_ERR_UNSUPPORTED),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+])
+def test_gqa_forward_validation(kw, expect):
+    assert _fwd_gqa(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=4 * 4 * 16 - 1), fa.FA_ERR_WORKSPACE),  # below D for every query row
+])
+def test_gqa_backward_validation(kw, expect):
+    assert _bwd_gqa(**kw) == expect
+
+
+def test_gqa_empty_calls_are_ok_without_pointers():
+    L = fa.lib()
+    assert L.fa_fwd_gqa(None, None, None, None, None, 1, 4, 2, 0, 64, 0.125, 0, None, None,
+                        fa.FA_BF16, fa.FA_BF16) == fa.FA_OK
+    assert L.fa_bwd_gqa(None, None, None, None, None, None, None, None, None, 0, 4, 2, 16, 64,
+                        0.125, 0, None, None, 0, None, fa.FA_BF16) == fa.FA_OK
+    # the head counts are checked even when there is nothing to compute
+    assert L.fa_fwd_gqa(None, None, None, None, None, 1, 4, 3, 0, 64, 0.125, 0, None, None,
+                        fa.FA_BF16, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+
+
+def test_gqa_workspace_sizes():
+    ws = fa.fa_bwd_gqa_workspace_bytes
+    # enough K/V heads to fill the chip: D for every query row only
+    assert ws(64, 32, 8, 4096, 128) == 64 * 32 * 4096 * 4
+    # one K/V head (multi-query): the group is shared among workgroups, whose
+    # fp32 partial dK and dV follow D (rounded up to 256 bytes)
+    B, H, Hkv, N, d = 2, 32, 1, 4096, 128
+    got = ws(B, H, Hkv, N, d)
+    dsum = B * H * N * 4
+    part = 2 * B * Hkv * N * d * 4
+    assert got > dsum and (got - dsum) % part == 0
+    shares = (got - dsum) // part
+    assert shares > 1 and H // Hkv % shares == 0
+    for bad in ((1, 4, 3, 16, 64), (1, 4, 0, 16, 64), (-1, 4, 2, 16, 64), (1, 4, 2, 16, 96)):
+        assert ws(*bad) == 0
