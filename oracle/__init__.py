@@ -6,7 +6,9 @@ this package. The library (``exact_io_aware_07_amd``) never imports it and
 shares no code with it; the two meet only at the seeded input generator.
 """
 from .attention import attn_bwd64, attn_bwd64_sampled, attn_fwd64, attn_probs64, visible_mask  # noqa: F401
-from .brute import brute_head_forward, brute_head_grad_fd, brute_head_part, brute_loss  # noqa: F401
+from .brute import (brute_head_allowed, brute_head_forward, brute_head_grad_fd,  # noqa: F401
+                    brute_head_part, brute_loss, brute_loss_allowed)
 from .memory import score_matrix_bytes  # noqa: F401
 from .split import attn_part64, merge64  # noqa: F401
 from .gqa import attn_bwd64_gqa, attn_fwd64_gqa  # noqa: F401
+from .sparse import attn_bwd64_sparse, attn_fwd64_sparse, sparse_visible  # noqa: F401

@@ -103,3 +103,34 @@ def brute_head_part(q, k, v, scale: float, causal: bool = False, q_pos0: int = 0
                        for c in range(dv)])
         lse.append(mx + math.log(tot))
     return o_rows, lse
+
+
+def brute_head_allowed(q, k, v, scale: float, allowed) -> Tuple[Matrix, List[float]]:
+    """One head with an explicit visibility table: key j is visible to query
+    i iff allowed[i][j]. Returns (O rows, LSE per row); a row with no visible
+    key gives O = 0 and LSE = -inf."""
+    q, k, v = _as_rows(q), _as_rows(k), _as_rows(v)
+    dv = len(v[0]) if v else len(q[0])
+    o_rows: Matrix = []
+    lse: List[float] = []
+    for i, qi in enumerate(q):
+        keys = [j for j in range(len(k)) if allowed[i][j]]
+        if not keys:
+            o_rows.append([0.0] * dv)
+            lse.append(-math.inf)
+            continue
+        s = [scale * math.fsum(qi[c] * k[j][c] for c in range(len(qi))) for j in keys]
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        tot = math.fsum(e)
+        o_rows.append([math.fsum(e[t] * v[j][c] for t, j in enumerate(keys)) / tot
+                       for c in range(dv)])
+        lse.append(mx + math.log(tot))
+    return o_rows, lse
+
+
+def brute_loss_allowed(q, k, v, do, scale: float, allowed) -> float:
+    """L = sum_ic dO_ic * O_ic for ``brute_head_allowed``."""
+    o, _ = brute_head_allowed(q, k, v, scale, allowed)
+    do = _as_rows(do)
+    return math.fsum(do[i][c] * o[i][c] for i in range(len(o)) for c in range(len(o[i])))
