@@ -236,6 +236,7 @@ def run_gpu(args):
         out["extra"] = extra_configs(torch, W)
         out["extra"][W.FEW_HEADS.name] = split_config(torch, W)
         out["extra"][W.GQA.name] = gqa_config(torch, W)
+        out["extra"][W.SPARSE.name] = sparse_config(torch, W)
     return out
 
 
@@ -256,6 +257,49 @@ def median_ms(torch, fn, iters: int = 10) -> float:
         torch.cuda.synchronize()
         batches.append(s.elapsed_time(e) / iters)
     return statistics.median(batches)
+
+
+def sparse_config(torch, W):
+    """Block-sparse attention on its band-and-first-block mask: forward and
+    backward through fa_fwd_sparse / fa_bwd_sparse, TFLOP/s counted on the
+    kept (query, key) pairs only, and the dense entry points on the same
+    inputs for the speed-up (ideal: 1 / kept fraction)."""
+    from exact_io_aware_07_amd import fa_bwd, fa_bwd_sparse, fa_fwd, fa_fwd_sparse
+    w = W.SPARSE
+    inp = W.make_inputs(w)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    mask = W.block_mask(w).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(w.B * w.H * w.N * 4, dtype=torch.uint8, device="cuda")
+    # kept pairs: every kept 128 x 128 block is whole (N is a multiple of 128)
+    kept = float(mask.sum().item()) * W.MASK_BLOCK * W.MASK_BLOCK * w.B * w.H
+    fwd_kept = 4.0 * w.d * kept
+    fa_fwd_sparse(q, k, v, o, lse, mask, w.scale, w.causal)
+    runs = {
+        "fwd_sparse": (lambda: fa_fwd_sparse(q, k, v, o, lse, mask, w.scale, w.causal), 1.0),
+        "bwd_sparse": (lambda: fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, mask, w.scale,
+                                             w.causal, None, ws), 2.5),
+    }
+    entry = {"kept_fraction": kept / (w.B * w.H * w.N * w.N), "mask": w.block_pattern}
+    for name, (fn, mult) in runs.items():
+        ms = median_ms(torch, fn)
+        rate = mult * fwd_kept / (ms * 1e-3)
+        entry[f"{name}_ms"] = ms
+        entry[f"{name}_tflops_on_kept_pairs"] = rate / 1e12
+        entry[f"{name}_pct_of_bf16_peak"] = 100 * rate / PEAK_BF16_FLOPS
+    o2, lse2 = torch.empty_like(q), torch.empty_like(lse)
+    fa_fwd(q, k, v, o2, lse2, w.scale, w.causal)
+    dense = {"fwd_dense_ms": lambda: fa_fwd(q, k, v, o2, lse2, w.scale, w.causal),
+             "bwd_dense_ms": lambda: fa_bwd(q, k, v, o2, do, lse2, dq, dk, dv, w.scale, w.causal,
+                                            None, ws)}
+    for name, fn in dense.items():
+        entry[name] = median_ms(torch, fn)
+    entry["fwd_speedup_vs_dense"] = entry["fwd_dense_ms"] / entry["fwd_sparse_ms"]
+    entry["bwd_speedup_vs_dense"] = entry["bwd_dense_ms"] / entry["bwd_sparse_ms"]
+    log(f"[bench] extra {w.name}: {entry}")
+    return entry
 
 
 def gqa_config(torch, W):

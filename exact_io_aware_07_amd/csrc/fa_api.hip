@@ -40,14 +40,17 @@ fa::Elem elem(int t) {
 int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, float* dsum, const int* kv_len,
                int B, int H, int N, int d, float scale, int causal, void* stream, int dtype,
-               int stages, int Hkv = 0, int gsplit = 1, float* dkv_part = nullptr) {
+               int stages, int Hkv = 0, int gsplit = 1, float* dkv_part = nullptr,
+               const unsigned char* bmask = nullptr, long long bm_sb = 0, long long bm_sh = 0) {
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dsum, kv_len, B, H, N, d, scale, causal,
-                Hkv > 0 ? Hkv : H, gsplit, dkv_part};
+                Hkv > 0 ? Hkv : H, gsplit, dkv_part, bmask, bm_sb, bm_sh};
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = (dtype == FA_F32) ? fa::launch_bwd_f32(a, stages, s)
-                                   : fa::launch_bwd_mfma(a, elem(dtype), stages, s);
+  hipError_t e = bmask ? fa::launch_bwd_mfma_sparse(a, elem(dtype), stages, s)
+                 : (dtype == FA_F32) ? fa::launch_bwd_f32(a, stages, s)
+                                     : fa::launch_bwd_mfma(a, elem(dtype), stages, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
 
 // Key split of a key-split forward: keys per part (a multiple of the
 // kernels' 64-key tile) and the number of parts that covers N.
@@ -319,6 +322,56 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
   return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d,
                     scale, causal, stream, dtype,
                     (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV, Hkv, gsplit, part);
+}
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, int d, float scale, int causal, const int* kv_len,
+                  const unsigned char* block_mask, long long mask_stride_b,
+                  long long mask_stride_h, void* stream, int in_dtype, int o_dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  // a mask row or column must fit the kernels' LDS list of kept blocks
+  if ((N + fa::kMaskBlock - 1) / fa::kMaskBlock > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  if (!block_mask) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0, H,
+                block_mask, mask_stride_b, mask_stride_h};
+  hipError_t e = fa::launch_fwd_mfma_sparse(a, elem(in_dtype), elem(o_dtype), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                  float scale, int causal, const int* kv_len, const unsigned char* block_mask,
+                  long long mask_stride_b, long long mask_stride_h, void* workspace,
+                  size_t workspace_bytes, void* stream, int dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  // a mask row or column must fit the kernels' LDS list of kept blocks
+  if ((N + fa::kMaskBlock - 1) / fa::kMaskBlock > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  if (!block_mask) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d,
+                    scale, causal, stream, dtype,
+                    (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV, H, 1, nullptr, block_mask,
+                    mask_stride_b, mask_stride_h);
 }
 
 const char* fa_strerror(int status) {

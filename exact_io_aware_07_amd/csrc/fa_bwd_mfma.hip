@@ -82,7 +82,9 @@ struct DkdvCfg {
   static constexpr int MINW = (D == 128) ? 1 : 2;  // waves per SIMD the registers allow
 };
 
-template <typename T, int D>
+// SP: block-sparse, only the query tiles of the query blocks the block mask
+// keeps against this key block (no grouped K/V heads).
+template <typename T, int D, bool SP>
 __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(BwdArgs a) {
   using L = TileLayout<D>;
   constexpr int BK = 32 * kBwdWaves;  // keys per workgroup
@@ -107,6 +109,8 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   auto gbuf = [&](int p) -> unsigned char* { return p ? Gs1 : Gs0; };
   auto lbuf = [&](int p) -> float* { return p ? Ls1 : Ls0; };
   auto dbuf = [&](int p) -> float* { return p ? Ds1 : Ds0; };
+  __shared__ unsigned short blist[SP ? kMaxMaskBlocks + 2 : 1];
+  __shared__ int bwc[SP ? kBwdWaves : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,6 +174,24 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   const int qt_end = (blk_key0 < kv_end) ? (N + BQ - 1) / BQ : qt_begin;
   const float sl2 = a.scale * kLog2e;
 
+  // Query tiles run as a sequence c in [c_begin, c_end), tile tile_ix(c):
+  // all tiles from qt_begin, or (block-sparse) only those of the query
+  // blocks kept against this key block, in increasing order.
+  int c_begin = qt_begin, c_end = qt_end, n_kept = 0;
+  if constexpr (SP) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mcol = a.bmask + (long long)b * a.bm_sb +
+                                (long long)(bhk - b * a.Hkv) * a.bm_sh + kb;
+    // BK is the mask block, so qt_begin is even: block qt_begin / 2 starts it.
+    n_kept = list_mask_blocks<kBwdThreads>(mcol, nb, qt_begin / 2, (qt_end + 1) / 2, blist, bwc);
+    c_begin = 0;
+    c_end = mask_tiles_below(blist, n_kept, qt_end);
+  }
+  auto tile_ix = [&](int c) -> int {
+    if constexpr (SP) return mask_tile(blist, c);
+    else return c;
+  };
+
   // Row-major fragment reads (A of S and dP): row qs*32 + kl, chunk 2dc + hh.
   int r_off[DC];
 #pragma unroll
@@ -204,10 +226,10 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   };
 
   auto prologue = [&]() {
-    if (qt_begin < qt_end) {
-      load_tiles(qt_begin, qt_begin & 1);
-      load_stats(qt_begin);
-      store_stats(qt_begin & 1);
+    if (c_begin < c_end) {
+      load_tiles(tile_ix(c_begin), c_begin & 1);
+      load_stats(tile_ix(c_begin));
+      store_stats(c_begin & 1);
     }
     // Unconditional, so that on every path into the loops below the K and
     // V fragment loads above are known complete: the compiler places waits
@@ -221,17 +243,18 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   // sub-tiles sit in one basic block. Queries past N need no mask anywhere:
   // their Q and dO rows read as zero and their LSE and D as zero, so their P
   // meets a zero dO row and their dS is zero.
-  auto tile = [&](int it, auto full, int buf) {
+  auto tile = [&](int c, auto full, int buf) {
     constexpr bool FULL = decltype(full)::value;
-    // Tile it has landed everywhere; every wave is done with tile it-1, so
-    // the other buffers are free for tile it+1.
+    // Tile c has landed everywhere; every wave is done with tile c-1, so
+    // the other buffers are free for tile c+1.
     __syncthreads();
-    const bool more = it + 1 < qt_end;
+    const bool more = c + 1 < c_end;
     if (more) {
-      load_tiles(it + 1, buf ^ 1);
-      load_stats(it + 1);
+      const int nxt = tile_ix(c + 1);
+      load_tiles(nxt, buf ^ 1);
+      load_stats(nxt);
     }
-    const int q0 = it * BQ;
+    const int q0 = tile_ix(c) * BQ;
     const bool live = FULL || ((key0 < kv_end) && (!a.causal || q0 + BQ - 1 >= key0));
     if (live) {
       // Full tiles: let the scheduler interleave the four MFMA chains with
@@ -294,21 +317,23 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   int it_full = qt_end;
   if (blk_key0 + BK <= kv_end) it_full = a.causal ? max(qt_begin, (blk_key0 + BK - 1 + BQ - 1) / BQ) : qt_begin;
   it_full = min(it_full, qt_end);
+  int c_full = it_full;  // sequence position of the first full tile
+  if constexpr (SP) c_full = mask_tiles_below(blist, n_kept, it_full);
   for (int g = g0; g < g1; ++g) {
     set_query_head(g);
     // Every wave is done with the previous query head's last tile before
     // this head's first tile is copied into the buffers.
     if (g > g0) __syncthreads();
     prologue();
-    int it = qt_begin;
-    for (; it < it_full; ++it) tile(it, Part{}, it & 1);
+    int c = c_begin;
+    for (; c < c_full; ++c) tile(c, Part{}, c & 1);
     // Full tiles in pairs of known parity (an odd first tile on its own).
-    if (it < qt_end && (it & 1)) tile(it++, Full{}, 1);
-    for (; it + 1 < qt_end; it += 2) {
-      tile(it, Full{}, 0);
-      tile(it + 1, Full{}, 1);
+    if (c < c_end && (c & 1)) tile(c++, Full{}, 1);
+    for (; c + 1 < c_end; c += 2) {
+      tile(c, Full{}, 0);
+      tile(c + 1, Full{}, 1);
     }
-    if (it < qt_end) tile(it, Full{}, 0);
+    if (c < c_end) tile(c, Full{}, 0);
   }
 
   // dK^T / dV^T accumulators: lane = key, registers = d in runs of 4.
@@ -368,7 +393,9 @@ struct DqCfg {
   static constexpr int MINW = (D == 64) ? 3 : 2;  // waves per SIMD the registers allow
 };
 
-template <typename T, int D>
+// SP: block-sparse, only the key tiles of the key blocks the block mask
+// keeps for this query block.
+template <typename T, int D, bool SP>
 __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs a) {
   using L = TileLayout<D>;
   constexpr int BR = 32 * kBwdWaves;
@@ -386,6 +413,8 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   __shared__ __attribute__((aligned(1024))) unsigned char Vs1[TB];
   auto kbuf = [&](int p) -> unsigned char* { return p ? Ks1 : Ks0; };
   auto vbuf = [&](int p) -> unsigned char* { return p ? Vs1 : Vs0; };
+  __shared__ unsigned short blist[SP ? kMaxMaskBlocks + 2 : 1];
+  __shared__ int bwc[SP ? kBwdWaves : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -413,13 +442,30 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   const int q_blk0 = qb * BR;
   int kv_lim = kv_end;
   if (a.causal) kv_lim = min(kv_lim, min(q_blk0 + BR, N));
-  const int ntiles = (kv_lim + BC - 1) / BC;
+  int ntiles = (kv_lim + BC - 1) / BC;
 
   const int wq0 = q_blk0 + wave * 32;
   const int my_q = wq0 + ql;
   int w_lim = kv_end;
   if (a.causal) w_lim = min(w_lim, min(wq0 + 31, N - 1) + 1);
-  const int w_tiles = (w_lim + BC - 1) / BC;
+  int w_tiles = (w_lim + BC - 1) / BC;
+
+  // Block-sparse: tile counts and positions j count only the tiles of the
+  // kept key blocks, in increasing order; tile_ix(j) is the key tile.
+  int n_kept = 0;
+  if constexpr (SP) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mrow = a.bmask + (long long)b * a.bm_sb +
+                                (long long)(bh - b * a.H) * a.bm_sh + (long long)qb * nb;
+    n_kept = list_mask_blocks<kBwdThreads>(mrow, 1, 0, min(nb, (kv_lim + kMaskBlock - 1) / kMaskBlock),
+                                           blist, bwc);
+    w_tiles = mask_tiles_below(blist, n_kept, w_tiles);
+    ntiles = mask_tiles_below(blist, n_kept, ntiles);
+  }
+  auto tile_ix = [&](int j) -> int {
+    if constexpr (SP) return mask_tile(blist, j);
+    else return j;
+  };
 
   u32x4 qf[DC], gf[DC];
 #pragma unroll
@@ -462,8 +508,12 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  auto load_k = [&](int j, int p) { load_tile_lds<D, BC, kBwdWaves>(rk, kbuf(p), j * BC, wave, lane); };
-  auto load_v = [&](int j, int p) { load_tile_lds<D, BC, kBwdWaves>(rv, vbuf(p), j * BC, wave, lane); };
+  auto load_k = [&](int j, int p) {
+    load_tile_lds<D, BC, kBwdWaves>(rk, kbuf(p), tile_ix(j) * BC, wave, lane);
+  };
+  auto load_v = [&](int j, int p) {
+    load_tile_lds<D, BC, kBwdWaves>(rv, vbuf(p), tile_ix(j) * BC, wave, lane);
+  };
   auto compute_sdp = [&](int p, f32x16 (&s)[KT], f32x16 (&dp)[KT]) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -500,7 +550,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
       if constexpr (FULL) __builtin_amdgcn_s_setprio(1);
       f32x16 s_cur[KT], p_cur[KT];
       compute_sdp(par, s_cur, p_cur);
-      const int t0 = j * BC;
+      const int t0 = tile_ix(j) * BC;
       const bool need_mask = !FULL && a.causal && t0 + BC - 1 > wq0;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
@@ -539,6 +589,9 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   // main loop; a full tile also loads the next one unconditionally, so it
   // must not be the last.
   int n_full = a.causal ? (q_blk0 + 1) / BC : ntiles;
+  if constexpr (SP) {
+    if (a.causal) n_full = mask_tiles_below(blist, n_kept, n_full);
+  }
   n_full = min(n_full, ntiles - 1);
   int j = 0;
   for (; j + 1 < n_full; j += 2) {
@@ -589,7 +642,7 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* __restrict
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool SP = false>
 hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   hipError_t e = hipSuccess;
   if (stages & (int)BwdStage::DSUM) {
@@ -601,13 +654,13 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   }
   if (stages & (int)BwdStage::DQ) {
     const long nqb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-    hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)((long)a.B * a.H * nqb)),
+    hipLaunchKernelGGL((dq_kernel<T, D, SP>), dim3((unsigned)((long)a.B * a.H * nqb)),
                        dim3(kBwdThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & (int)BwdStage::DKDV) {
     const long nkb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-    hipLaunchKernelGGL((dkdv_kernel<T, D>),
+    hipLaunchKernelGGL((dkdv_kernel<T, D, SP>),
                        dim3((unsigned)((long)a.B * a.Hkv * a.gsplit * nkb)), dim3(kBwdThreads),
                        0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -622,9 +675,9 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   return e;
 }
 
-template <typename T>
+template <typename T, bool SP = false>
 hipError_t launch_t(const BwdArgs& a, int stages, hipStream_t st) {
-  return (a.d == 128) ? launch<T, 128>(a, stages, st) : launch<T, 64>(a, stages, st);
+  return (a.d == 128) ? launch<T, 128, SP>(a, stages, st) : launch<T, 64, SP>(a, stages, st);
 }
 
 }  // namespace
@@ -641,6 +694,11 @@ int bwd_group_split(int B, int H, int Hkv, int N, int d) {
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, Elem t, int stages, hipStream_t st) {
   return (t == Elem::BF16) ? launch_t<BF16>(a, stages, st) : launch_t<F16>(a, stages, st);
+}
+
+hipError_t launch_bwd_mfma_sparse(const BwdArgs& a, Elem t, int stages, hipStream_t st) {
+  const int s = stages & ((int)BwdStage::DQ | (int)BwdStage::DKDV);
+  return (t == Elem::BF16) ? launch_t<BF16, true>(a, s, st) : launch_t<F16, true>(a, s, st);
 }
 
 }  // namespace fa

@@ -63,9 +63,11 @@ struct FwdTile {
 // GEN: the general form (key count, positions and key split from the
 // arguments); without it they are folded to the plain forward's (Nk = N,
 // equal positions, one split), so that path compiles as if they did not
-// exist.
-template <typename T, int D, bool OUT_F32, bool GEN>
+// exist. SP: block-sparse, the plain forward over the tiles of the key
+// blocks the block mask keeps for this query block (not with GEN).
+template <typename T, int D, bool OUT_F32, bool GEN, bool SP>
 __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(FwdArgs a) {
+  static_assert(!(GEN && SP), "the block-sparse form is the plain forward's");
   using L = TileLayout<D>;
   constexpr int BC = FwdTile<D>::BC;
   constexpr int KT = BC / 32;                   // 32-key sub-tiles
@@ -83,6 +85,9 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   // Buffer of parity p; p is a compile-time constant in the main loop.
   auto kbuf = [&](int p) -> unsigned char* { return p ? Ks1 : Ks0; };
   auto vbuf = [&](int p) -> unsigned char* { return p ? Vs1 : Vs0; };
+  // Block-sparse: the kept key blocks of this query block, listed.
+  __shared__ unsigned short blist[SP ? kMaxMaskBlocks + 2 : 1];
+  __shared__ int bwc[SP ? kWaves : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,13 +128,30 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   // Tiles are counted from this split's first tile jb (k_lo is a multiple of
   // the tile width); tile t holds keys [(jb + t) * BC, (jb + t + 1) * BC).
   const int jb = k_lo / BC;
-  const int ntiles = max((kv_lim + BC - 1) / BC - jb, 0);
+  int ntiles = max((kv_lim + BC - 1) / BC - jb, 0);
 
   const int wq0 = q_blk0 + wave * 32;
   const int my_q = wq0 + ql;
   int w_lim = kv_end;  // keys this wave needs (exclusive)
   if (a.causal) w_lim = min(w_lim, min(wq0 + 31, N - 1) + delta + 1);
-  const int w_tiles = max((max(w_lim, 0) + BC - 1) / BC - jb, 0);  // tiles this wave computes
+  int w_tiles = max((max(w_lim, 0) + BC - 1) / BC - jb, 0);  // tiles this wave computes
+
+  // Block-sparse: from here on a tile count or position t counts only the
+  // tiles of kept blocks, in increasing order; tile_ix(t) is the key tile.
+  int n_kept = 0;
+  if constexpr (SP) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mrow = a.bmask + (long long)b * a.bm_sb +
+                                (long long)(bh - b * a.H) * a.bm_sh + (long long)qb * nb;
+    n_kept = list_mask_blocks<kThreads>(mrow, 1, 0, min(nb, (kv_lim + kMaskBlock - 1) / kMaskBlock),
+                                        blist, bwc);
+    w_tiles = mask_tiles_below(blist, n_kept, w_tiles);
+    ntiles = mask_tiles_below(blist, n_kept, ntiles);
+  }
+  auto tile_ix = [&](int t) -> int {
+    if constexpr (SP) return mask_tile(blist, t);
+    else return jb + t;
+  };
 
   u32x4 qf[DC];
 #pragma unroll
@@ -143,7 +165,7 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   const float sl2 = a.scale * kLog2e;
 
   auto load_tile = [&](__amdgpu_buffer_rsrc_t r, unsigned char* dst, int t) {
-    load_tile_lds<D, BC, kWaves>(r, dst, (jb + t) * BC, wave, lane);
+    load_tile_lds<D, BC, kWaves>(r, dst, tile_ix(t) * BC, wave, lane);
   };
 
   // K fragment (A of S^T): row kt*32 + ql, chunk 2*dc + hh. The row's place
@@ -198,7 +220,7 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
     const bool live = FULL || j < w_tiles;
     if (live) {
       if constexpr (!FULL) {
-        const int t0 = (jb + j) * BC;
+        const int t0 = tile_ix(j) * BC;
         const bool need_mask = (t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0 + delta);
         if (need_mask) {
 #pragma unroll
@@ -285,7 +307,8 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   // Tiles fully visible to every row of the workgroup, and followed by a
   // further tile, form the branch-free main loop (an even count, so the two
   // S arrays swap roles without copies).
-  const int n_vis = (a.causal ? min(kv_end, q_blk0 + delta + 1) : kv_end) / BC - jb;
+  int n_vis = (a.causal ? min(kv_end, q_blk0 + delta + 1) : kv_end) / BC - jb;
+  if constexpr (SP) n_vis = mask_tiles_below(blist, n_kept, n_vis);
   const int n_full = max(min(n_vis, ntiles - 1), 0) & ~1;
   int j = 0;
   for (; j < n_full; j += 2) {
@@ -324,18 +347,20 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   }
 }
 
-template <typename T, int D, bool OF, bool GEN>
+template <typename T, int D, bool OF, bool GEN, bool SP = false>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   const long nqb = (a.N + kBR - 1) / kBR;
   const long total = (long)a.B * a.H * nqb * (GEN ? a.nsplit : 1);
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, OF, GEN>), dim3((unsigned)total), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, OF, GEN, SP>), dim3((unsigned)total), dim3(kThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool SP = false>
 hipError_t launch_t(const FwdArgs& a, bool of, hipStream_t s) {
-  if (a.d == 128) return of ? launch<T, 128, true, false>(a, s) : launch<T, 128, false, false>(a, s);
-  return of ? launch<T, 64, true, false>(a, s) : launch<T, 64, false, false>(a, s);
+  if (a.d == 128)
+    return of ? launch<T, 128, true, false, SP>(a, s) : launch<T, 128, false, false, SP>(a, s);
+  return of ? launch<T, 64, true, false, SP>(a, s) : launch<T, 64, false, false, SP>(a, s);
 }
 
 }  // namespace
@@ -344,6 +369,12 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, Elem in, Elem out, hipStream_t s) {
   const bool of = (out == Elem::F32);
   if (in == Elem::BF16) return launch_t<BF16>(a, of, s);
   return launch_t<F16>(a, of, s);
+}
+
+hipError_t launch_fwd_mfma_sparse(const FwdArgs& a, Elem in, Elem out, hipStream_t s) {
+  const bool of = (out == Elem::F32);
+  if (in == Elem::BF16) return launch_t<BF16, true>(a, of, s);
+  return launch_t<F16, true>(a, of, s);
 }
 
 hipError_t launch_fwd_mfma_general(const FwdArgs& a, Elem in, hipStream_t s) {

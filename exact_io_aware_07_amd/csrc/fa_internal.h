@@ -31,6 +31,11 @@ struct FwdArgs {
   // K/V heads (H for plain attention): query head h of a batch uses K/V head
   // h / (H / Hkv); K and V are [B, Hkv, Nk, d].
   int Hkv;
+  // Block mask of block-sparse attention (read only by that instantiation):
+  // entry (b, h, i, j) at bmask[b * bm_sb + h * bm_sh + i * nb + j], nb =
+  // ceil(N / kMaskBlock); nonzero keeps query block i against key block j.
+  const unsigned char* bmask;
+  long long bm_sb, bm_sh;
 };
 
 struct BwdArgs {
@@ -57,6 +62,9 @@ struct BwdArgs {
   // reduction then sums the parts into dk, dv. gsplit divides H / Hkv.
   int gsplit;
   float* dkv_part;
+  // Block mask, as in FwdArgs (block-sparse instantiations only).
+  const unsigned char* bmask;
+  long long bm_sb, bm_sh;
 };
 
 // Query-head split of the grouped dK/dV stage for a shape: the smallest
@@ -71,11 +79,23 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, Elem in, Elem out, hipStream_t s);
 // output; the plain forward above ignores those fields.
 hipError_t launch_fwd_mfma_general(const FwdArgs& a, Elem in, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+// Block-sparse forward: only the tiles of the key blocks bmask keeps.
+hipError_t launch_fwd_mfma_sparse(const FwdArgs& a, Elem in, Elem out, hipStream_t s);
+
+// Block-sparse attention: masks come in blocks of kMaskBlock queries by
+// kMaskBlock keys (the query block of the forward and dQ workgroups, the key
+// block of the dK/dV workgroup, two 64-row tiles each). A workgroup lists
+// the kept blocks of its mask row or column in LDS, so a row or column
+// holds at most kMaxMaskBlocks blocks.
+constexpr int kMaskBlock = 128;
+constexpr int kMaxMaskBlocks = 4096;
 // Backward stages, launched in this order when several are asked for: the
 // stand-alone D_i = rowsum(dO * O), then dQ (which also forms D_i for its
 // rows and writes it to the workspace), then dK/dV (which reads D_i).
 enum class BwdStage { DSUM = 1, DKDV = 2, DQ = 4, ALL = 7 };
 hipError_t launch_bwd_mfma(const BwdArgs& a, Elem t, int stages, hipStream_t s);
+// Block-sparse backward stages (DQ and DKDV), skipping the blocks bmask drops.
+hipError_t launch_bwd_mfma_sparse(const BwdArgs& a, Elem t, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
 
 // Merge of partial results (fp32 O [rows][d] and LSE [rows] per part) into
@@ -314,6 +334,61 @@ __device__ inline int causal_item(int bid, int total, int nblk, int nheads, int 
   const bool before = lane < kCusPerXcd && p < m && (l_p < l_me || (l_p == l_me && p < c));
   const int r = __popcll(__ballot(before));
   return 8 * (2 * kCusPerXcd + r) + x;
+}
+
+// The kept blocks among [lo, hi) of one block-mask row (stride 1) or column
+// (stride = blocks per row) starting at m, listed in increasing order in
+// list by the whole workgroup of NT threads (a ballot per wave, the waves'
+// counts through LDS). Two copies of the last kept block (or of block 0)
+// follow the list, so that a prefetch one or two tiles past its end reads a
+// tile of the head. Returns the count, the same in every thread.
+template <int NT>
+__device__ inline int list_mask_blocks(const unsigned char* __restrict__ m, long long stride, int lo,
+                                       int hi, unsigned short* list, int* wcount) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int base = 0;
+  for (int c0 = lo; c0 < hi; c0 += NT) {
+    const int blk = c0 + tid;
+    const bool on = blk < hi && m[(long long)blk * stride] != 0;
+    const unsigned long long bal = __ballot(on);
+    if (lane == 0) wcount[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = wcount[w];
+      off += (w < wave) ? c : 0;
+      tot += c;
+    }
+    if (on) list[off + __popcll(bal & ((1ull << lane) - 1))] = (unsigned short)blk;
+    base += tot;
+    // every wave has read wcount before the next round overwrites it
+    __syncthreads();
+  }
+  if (tid < 2) list[base + tid] = base > 0 ? list[base - 1] : (unsigned short)0;
+  __syncthreads();
+  return base;
+}
+
+// Tiles of a listed sequence (block b holds tiles 2b and 2b + 1) whose
+// index is below lim: the sequence position of the first tile at or past
+// lim. The list is increasing, so a binary search; the same in every lane.
+__device__ inline int mask_tiles_below(const unsigned short* list, int n, int lim) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (2 * (int)list[mid] < lim) lo = mid + 1;
+    else hi = mid;
+  }
+  return 2 * lo - ((lo > 0 && 2 * (int)list[lo - 1] + 1 >= lim) ? 1 : 0);
+}
+
+// Tile index of sequence position t (wave-uniform, in an SGPR).
+__device__ inline int mask_tile(const unsigned short* list, int t) {
+  return __builtin_amdgcn_readfirstlane(2 * (int)list[t >> 1] + (t & 1));
 }
 
 __device__ inline int xcd_remap(int bid, int total);

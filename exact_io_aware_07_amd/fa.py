@@ -21,7 +21,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0,
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_dsum", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_partial", "fa_merge", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split", "fa_fwd_gqa", "fa_bwd_gqa_workspace_bytes", "fa_bwd_gqa",
-           "fa_strerror")
+           "fa_fwd_sparse", "fa_bwd_sparse", "fa_strerror")
 
 _DTYPE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib: Optional[ctypes.CDLL] = None
@@ -69,6 +69,12 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz,
                              vp, i]
     L.fa_bwd_gqa.restype = i
+    ll = ctypes.c_longlong
+    L.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, ll, ll, vp, i, i]
+    L.fa_fwd_sparse.restype = i
+    L.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, ll,
+                                ll, vp, sz, vp, i]
+    L.fa_bwd_sparse.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -319,6 +325,67 @@ def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = F
                           _DTYPE.get(q.dtype, -99))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_gqa")
+
+
+def _mask_strides(block_mask, B: int, H: int, N: int):
+    """Element strides (batch, head) of a uint8 block mask shaped [nb, nb],
+    [H, nb, nb] or [B, H, nb, nb] (nb = ceil(N / 128)); a missing leading
+    axis, or one of extent 1, is shared (stride 0)."""
+    nb = (N + 127) // 128
+    if block_mask.dtype != torch.uint8:
+        raise ValueError("block_mask must be uint8")
+    if not block_mask.is_cuda or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous device tensor")
+    shp = tuple(block_mask.shape)
+    if len(shp) < 2 or shp[-2:] != (nb, nb):
+        raise ValueError(f"block_mask has shape {shp}, expected [..., {nb}, {nb}]")
+    lead = (1,) * (4 - len(shp)) + shp[:-2]
+    if len(lead) != 2 or lead[0] not in (1, B) or lead[1] not in (1, H):
+        raise ValueError(f"block_mask has shape {shp}, expected [B or 1, H or 1, {nb}, {nb}]")
+    sh = nb * nb if lead[1] == H and H > 1 else 0
+    sb = lead[1] * nb * nb if lead[0] == B and B > 1 else 0
+    return sb, sh
+
+
+def fa_fwd_sparse(q, k, v, o, lse, block_mask, scale: float, causal: bool = False, kv_len=None,
+                  stream=None) -> None:
+    """Enqueue block-sparse attention: like fa_fwd, restricted to the 128x128
+    (query block, key block) pairs ``block_mask`` (uint8, nonzero keeps)
+    keeps; see _mask_strides for its accepted shapes."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("o", o, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    sb, sh = _mask_strides(block_mask, B, H, N)
+    st = lib().fa_fwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                             float(scale), int(bool(causal)), _kv(kv_len, B), _ptr(block_mask),
+                             sb, sh, _stream(stream, q.device), _DTYPE.get(q.dtype, -99),
+                             _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_sparse")
+
+
+def fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, block_mask, scale: float,
+                  causal: bool = False, kv_len=None, workspace=None, stream=None) -> None:
+    """Enqueue the block-sparse backward (gradients of fa_fwd_sparse's output)."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    sb, sh = _mask_strides(block_mask, B, H, N)
+    need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_bwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                             _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                             _kv(kv_len, B), _ptr(block_mask), sb, sh, _ptr(workspace), ws_bytes,
+                             _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_sparse")
 
 
 # Convenience wrappers that allocate the outputs with torch (plumbing only).

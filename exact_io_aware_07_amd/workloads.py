@@ -50,6 +50,7 @@ class Workload:
     backward: bool = False
     measurement_only: bool = False
     Hkv: Optional[int] = None  # K/V heads (grouped-query attention); None means H
+    block_pattern: Optional[str] = None  # block-sparse mask (see block_mask); None means dense
     note: str = field(default="", compare=False)
 
     @property
@@ -107,8 +108,15 @@ GQA = Workload("long_context_gqa_bf16_causal_fwd_bwd", 2, 32, 4096, 128, "bf16",
                backward=True, measurement_only=True, Hkv=8,
                note="B=2 H=32 Hkv=8 N=4096 d=128 bf16 causal, forward + backward")
 
+# Block-sparse: 16 heads of 16,384 tokens where each 128-token query block
+# keeps its own key block, its two neighbours and the first key block (the
+# "band_sink" pattern of block_mask), 4 of 128 blocks per row.
+SPARSE = Workload("long_block_sparse_band_bf16_fwd_bwd", 1, 16, 16384, 64, "bf16",
+                  backward=True, measurement_only=True, block_pattern="band_sink",
+                  note="B=1 H=16 N=16384 d=64 bf16, 128x128 block mask: band of 3 + first block")
+
 CONFIGS: Dict[str, Workload] = {w.name: w for w in (TINY, BERT, LONG, TRADE, GPT2)}
-MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD, FEW_HEADS, GQA)}
+MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD, FEW_HEADS, GQA, SPARSE)}
 ALL: Dict[str, Workload] = {**CONFIGS, **MEASUREMENT}
 
 
@@ -180,3 +188,30 @@ def random_case(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     if kv_len is not None:
         out["kv_len"] = torch.tensor(kv_len, dtype=torch.int32)
     return out
+
+
+MASK_BLOCK = 128  # queries (and keys) per block of a block-sparse mask
+
+
+def block_mask(w: Workload) -> Optional[torch.Tensor]:
+    """The uint8 [nb, nb] block mask of a block-sparse workload (nb =
+    ceil(N / 128)), shared by every batch and head, or None for a dense one.
+
+    "band_sink": query block i keeps key blocks i - 1, i, i + 1 and 0.
+    """
+    if w.block_pattern is None:
+        return None
+    nb = (w.N + MASK_BLOCK - 1) // MASK_BLOCK
+    i = torch.arange(nb)[:, None]
+    j = torch.arange(nb)[None, :]
+    if w.block_pattern == "band_sink":
+        return (((i - j).abs() <= 1) | (j == 0)).to(torch.uint8)
+    raise ValueError(f"unknown block pattern {w.block_pattern!r}")
+
+
+def random_block_mask(lead: Tuple[int, ...], N: int, keep: float, seed: int) -> torch.Tensor:
+    """A seeded uint8 block mask of shape lead + (nb, nb): each block pair
+    kept with probability ``keep`` (one ``torch.rand`` draw per entry)."""
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (torch.rand(tuple(lead) + (nb, nb), generator=g) < keep).to(torch.uint8)

@@ -209,6 +209,39 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                const int* kv_len, void* workspace, size_t workspace_bytes,
                void* stream, int dtype);
 
+/*
+ * Block-sparse attention: attention restricted to the (query block, key
+ * block) pairs a block mask keeps; the tiles of dropped blocks are never
+ * loaded or computed. The pages present this as a separate variant that
+ * approximates full attention (Ultralytics glossary page "Flash
+ * Attention", section "Flash Attention e termini correlati"; delect.ru
+ * glossary page "FlashAttention", section "Что подтверждено"). On the kept
+ * pairs the result is exact: key j is visible to query i when the mask
+ * keeps block pair (i / 128, j / 128) and kv_len and causal (as for fa_fwd)
+ * allow it; a row with no visible key gets O = 0, LSE = -inf and zero
+ * gradients.
+ *   block_mask  device uint8; entry (b, h, I, J) at
+ *               block_mask[b * mask_stride_b + h * mask_stride_h + I * nb + J],
+ *               nb = ceil(N / 128), blocks of 128 queries by 128 keys;
+ *               nonzero keeps the pair. Strides are element counts >= 0 (0
+ *               shares one mask among batches or heads).
+ * Other arguments and the workspace (fa_bwd_workspace_bytes) are as for
+ * fa_fwd / fa_bwd. fp16/bf16 only (FA_F32 returns FA_ERR_UNSUPPORTED).
+ * nb <= 4096 (N <= 524288), else FA_ERR_UNSUPPORTED; a NULL mask or a
+ * negative stride returns FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, float scale, int causal,
+                  const int* kv_len, const unsigned char* block_mask,
+                  long long mask_stride_b, long long mask_stride_h, void* stream,
+                  int in_dtype, int o_dtype);
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  int B, int H, int N, int d, float scale, int causal,
+                  const int* kv_len, const unsigned char* block_mask,
+                  long long mask_stride_b, long long mask_stride_h, void* workspace,
+                  size_t workspace_bytes, void* stream, int dtype);
+
 /* Static, human-readable text for a status code. Never NULL. */
 const char* fa_strerror(int status);
 

@@ -11,4 +11,5 @@ from .brute import (brute_head_allowed, brute_head_forward, brute_head_grad_fd, 
 from .memory import score_matrix_bytes  # noqa: F401
 from .split import attn_part64, merge64  # noqa: F401
 from .gqa import attn_bwd64_gqa, attn_fwd64_gqa  # noqa: F401
-from .sparse import attn_bwd64_sparse, attn_fwd64_sparse, sparse_visible  # noqa: F401
+from .sparse import (attn_bwd64_sparse, attn_bwd64_sparse_sampled, attn_fwd64_sparse,  # noqa: F401
+                     sparse_visible)

@@ -23,14 +23,16 @@ import numpy as np
 
 from .attention import _f64, _kv_lens
 
-__all__ = ["sparse_visible", "attn_fwd64_sparse", "attn_bwd64_sparse"]
+__all__ = ["sparse_visible", "attn_fwd64_sparse", "attn_bwd64_sparse", "attn_bwd64_sparse_sampled"]
 
 
-def sparse_visible(N: int, causal: bool, kv_len_b: int, mask_bh, block: int) -> np.ndarray:
-    """Boolean [N, N]: True where key j is visible to query i for one head
-    whose block mask is ``mask_bh`` ([ceil(N/block), ceil(N/block)])."""
-    i = np.arange(N)[:, None]
-    j = np.arange(N)[None, :]
+def sparse_visible(N: int, causal: bool, kv_len_b: int, mask_bh, block: int,
+                   rows=None, cols=None) -> np.ndarray:
+    """Boolean [R, C]: True where key j is visible to query i for one head
+    whose block mask is ``mask_bh`` ([ceil(N/block), ceil(N/block)]); rows
+    and cols (default: all N) pick the queries i and keys j."""
+    i = (np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64))[:, None]
+    j = (np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64))[None, :]
     m = np.asarray(mask_bh) != 0
     vis = m[i // block, j // block] & (j < kv_len_b)
     if causal:
@@ -55,19 +57,26 @@ def _mask_of(block_mask, b: int, h: int):
     return m[b, h] if m.ndim == 4 else m
 
 
-def attn_fwd64_sparse(q, k, v, scale: float, causal: bool, kv_len, block_mask, block: int = 128):
+def attn_fwd64_sparse(q, k, v, scale: float, causal: bool, kv_len, block_mask, block: int = 128,
+                      rows=None, row_chunk: int = 1024):
     """q, k, v: [B, H, N, d]; block_mask: [B, H, nb, nb] or [nb, nb] (one mask
-    for every head), nb = ceil(N / block). Returns (O [B, H, N, d], LSE [B, H, N])."""
+    for every head), nb = ceil(N / block). ``rows`` restricts the output to
+    those query rows (all keys still used), taken ``row_chunk`` at a time.
+    Returns (O [B, H, R, d], LSE [B, H, R])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
     lens = _kv_lens(kv_len, B, N)
-    o = np.zeros((B, H, N, d))
-    lse = np.zeros((B, H, N))
+    rr = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((B, H, len(rr), d))
+    lse = np.zeros((B, H, len(rr)))
     for b in range(B):
         for h in range(H):
-            vis = sparse_visible(N, causal, int(lens[b]), _mask_of(block_mask, b, h), block)
-            p, lse[b, h] = _probs(q[b, h], k[b, h], vis, scale)
-            o[b, h] = p @ v[b, h]
+            for c0 in range(0, len(rr), row_chunk):
+                part = rr[c0:c0 + row_chunk]
+                vis = sparse_visible(N, causal, int(lens[b]), _mask_of(block_mask, b, h), block,
+                                     rows=part)
+                p, lse[b, h, c0:c0 + len(part)] = _probs(q[b, h, part], k[b, h], vis, scale)
+                o[b, h, c0:c0 + len(part)] = p @ v[b, h]
     return o, lse
 
 
@@ -89,4 +98,49 @@ def attn_bwd64_sparse(q, k, v, dout, scale: float, causal: bool, kv_len, block_m
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def attn_bwd64_sparse_sampled(q, k, v, dout, scale: float, causal: bool, kv_len, block_mask,
+                              heads, q_rows, k_rows, block: int = 128, row_chunk: int = 1024):
+    """The gradients of ``attn_bwd64_sparse`` on sampled query rows (dQ) and
+    keys (dK, dV) of the listed (b, h) heads, for N too long for an N x N
+    matrix. Per head, LSE_i and D_i = sum_j P_ij dP_ij come from whole rows
+    taken ``row_chunk`` at a time; then
+      dQ_i = scale sum_j P_ij (dP_ij - D_i) K_j   (whole rows i in q_rows)
+      dK_j = scale sum_i P_ij (dP_ij - D_i) Q_i   (whole columns j in k_rows)
+      dV_j = sum_i P_ij dO_i
+    with P_ij = exp(S_ij - LSE_i) on the visible set and 0 elsewhere.
+    Returns (dQ [len(heads), R, d], dK [len(heads), C, d], dV [len(heads), C, d])."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    lens = _kv_lens(kv_len, B, N)
+    qr = np.asarray(q_rows, dtype=np.int64)
+    kr = np.asarray(k_rows, dtype=np.int64)
+    dq = np.zeros((len(heads), len(qr), d))
+    dk = np.zeros((len(heads), len(kr), d))
+    dv = np.zeros((len(heads), len(kr), d))
+    for t, (b, h) in enumerate(heads):
+        m = _mask_of(block_mask, b, h)
+        lim = int(lens[b])
+        lse = np.empty(N)
+        dsum = np.empty(N)
+        for c0 in range(0, N, row_chunk):
+            part = np.arange(c0, min(c0 + row_chunk, N))
+            vis = sparse_visible(N, causal, lim, m, block, rows=part)
+            p, lse[part] = _probs(q[b, h, part], k[b, h], vis, scale)
+            dsum[part] = (p * (dout[b, h, part] @ v[b, h].T)).sum(axis=1)
+        if len(qr):
+            vis = sparse_visible(N, causal, lim, m, block, rows=qr)
+            p, _ = _probs(q[b, h, qr], k[b, h], vis, scale)
+            dp = dout[b, h, qr] @ v[b, h].T
+            dq[t] = scale * ((p * (dp - dsum[qr, None])) @ k[b, h])
+        if len(kr):
+            vis = sparse_visible(N, causal, lim, m, block, cols=kr)
+            has = np.isfinite(lse)
+            s_c = scale * (q[b, h] @ k[b, h, kr].T)
+            p = np.where(vis & has[:, None], np.exp(s_c - np.where(has, lse, 0.0)[:, None]), 0.0)
+            ds = p * (dout[b, h] @ v[b, h, kr].T - dsum[:, None])
+            dk[t] = scale * (ds.T @ q[b, h])
+            dv[t] = p.T @ dout[b, h]
     return dq, dk, dv

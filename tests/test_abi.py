@@ -304,3 +304,46 @@ def test_gqa_workspace_sizes():
     assert shares > 1 and H // Hkv % shares == 0
     for bad in ((1, 4, 3, 16, 64), (1, 4, 0, 16, 64), (-1, 4, 2, 16, 64), (1, 4, 2, 16, 96)):
         assert ws(*bad) == 0
+
+
+def _fwd_sp(q=A, mask=A, B=1, H=2, N=300, d=64, sb=0, sh=9, causal=0, it=fa.FA_BF16, ot=fa.FA_BF16):
+    return fa.lib().fa_fwd_sparse(q, A, A, A, A, B, H, N, d, 0.125, causal, None, mask, sb, sh, None,
+                                  it, ot)
+
+
+def _bwd_sp(mask=A, ws=A, ws_bytes=1 << 20, B=1, H=2, N=300, d=64, sb=0, sh=9, dtype=fa.FA_BF16):
+    return fa.lib().fa_bwd_sparse(A, A, A, A, A, A, A, A, A, B, H, N, d, 0.125, 0, None, mask, sb,
+                                  sh, ws, ws_bytes, None, dtype)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(mask=None), fa.FA_ERR_INVALID_ARG),
+    (dict(sb=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(sh=-9), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(it=fa.FA_F32, ot=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=128 * 4096 + 1), fa.FA_ERR_UNSUPPORTED),  # a mask row longer than the LDS list
+])
+def test_sparse_forward_validation(kw, expect):
+    assert _fwd_sp(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(mask=None), fa.FA_ERR_INVALID_ARG),
+    (dict(sh=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=2 * 300 * 4 - 1), fa.FA_ERR_WORKSPACE),
+    (dict(N=128 * 4096 + 1), fa.FA_ERR_UNSUPPORTED),
+])
+def test_sparse_backward_validation(kw, expect):
+    assert _bwd_sp(**kw) == expect
+
+
+def test_sparse_empty_calls_need_no_pointers():
+    L = fa.lib()
+    assert L.fa_fwd_sparse(None, None, None, None, None, 0, 2, 300, 64, 0.125, 0, None, None, 0, 0,
+                           None, fa.FA_BF16, fa.FA_BF16) == fa.FA_OK
+    assert L.fa_bwd_sparse(None, None, None, None, None, None, None, None, None, 1, 2, 0, 64, 0.125,
+                           0, None, None, 0, 0, None, 0, None, fa.FA_BF16) == fa.FA_OK

@@ -1,0 +1,165 @@
+"""GPU parity of block-sparse attention (fa_fwd_sparse, fa_bwd_sparse) through
+the C ABI, against the fp64 oracle (oracle/sparse.py).
+
+Exact properties checked besides the oracle: a mask that keeps every block
+gives fa_fwd / fa_bwd bit for bit (the kernels then visit the same tiles in
+the same order), and so does a causal mask keeping the blocks on and below
+the diagonal; one mask shared by all heads (stride 0) gives the same bits
+as that mask copied per head.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_07_amd import fa_bwd, fa_bwd_sparse, fa_fwd, fa_fwd_sparse
+from exact_io_aware_07_amd import workloads as W
+from helpers import (FWD_MAX_ABS, FWD_MEAN_ABS, GRAD_REL_FRO, LSE_MAX_ABS, dev, fwd_stats, np64,
+                     rel_fro, say)
+from oracle import attn_bwd64_sparse, attn_bwd64_sparse_sampled, attn_fwd64_sparse
+
+pytestmark = pytest.mark.gpu
+
+
+def run(inp, mask, scale, causal, out_dtype=None, backward=True):
+    q, k, v, do, kv = (dev(inp[n]) for n in ("q", "k", "v", "do", "kv_len"))
+    m = mask.contiguous().cuda()
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    fa_fwd_sparse(q, k, v, o, lse, m, scale, causal, kv)
+    grads = None
+    if backward:
+        o_in = o if o.dtype == q.dtype else o.to(q.dtype)
+        grads = [torch.empty_like(q) for _ in range(3)]
+        fa_bwd_sparse(q, k, v, o_in, do, lse, *grads, m, scale, causal, kv)
+    torch.cuda.synchronize()
+    return o, lse, grads
+
+
+def check_fwd(o, lse, o_ref, lse_ref):
+    st = fwd_stats(np64(o), np64(lse), o_ref, lse_ref)
+    assert st["max_abs"] <= FWD_MAX_ABS and st["mean_abs"] <= FWD_MEAN_ABS, st
+    assert st["lse_max_abs"] <= LSE_MAX_ABS, st
+
+
+def check_grads(grads, ref, label):
+    errs = {n: rel_fro(np64(g), r) for n, g, r in zip(("dq", "dk", "dv"), grads, ref)}
+    print(f"{label} rel-fro {errs}", flush=True)
+    for n, e in errs.items():
+        assert e <= GRAD_REL_FRO, (n, e)
+
+
+# (B, H, N, d, keep): ragged N, one to eight mask blocks, both head dims
+SHAPES = [
+    (2, 2, 300, 64, 0.5),
+    (1, 3, 520, 128, 0.5),
+    (2, 1, 129, 64, 0.7),
+    (1, 2, 1000, 64, 0.3),
+    (1, 2, 1024, 128, 0.6),
+    (3, 1, 100, 64, 1.0),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_sparse_matches_oracle(shape, causal, dtype):
+    B, H, N, d, keep = shape
+    say(f"sparse fwd+bwd {shape} causal={causal} {dtype}")
+    inp = W.random_case(B, H, N, d, dtype, seed=N + d, causal=causal, backward=True)
+    mask = W.random_block_mask((B, H), N, keep, seed=N + 1)
+    o, lse, grads = run(inp, mask, d ** -0.5, causal, out_dtype=torch.float32)
+    o_ref, lse_ref = attn_fwd64_sparse(inp["q"], inp["k"], inp["v"], d ** -0.5, causal, None, mask.numpy())
+    check_fwd(o, lse, o_ref, lse_ref)
+    ref = attn_bwd64_sparse(inp["q"], inp["k"], inp["v"], inp["do"], d ** -0.5, causal, None, mask.numpy())
+    check_grads(grads, ref, str(shape))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sparse_key_padding_and_empty_rows(causal):
+    B, H, N, d = 4, 2, 400, 64
+    kv_len = [0, 1, 200, 400]
+    say(f"sparse kv_len {kv_len} causal={causal}")
+    inp = W.random_case(B, H, N, d, "bf16", seed=5, causal=causal, kv_len=kv_len, backward=True)
+    mask = W.random_block_mask((B, H), N, 0.5, seed=6)
+    mask[:, :, 1, :] = 0  # query block 1 keeps nothing: its rows have no visible key
+    o, lse, grads = run(inp, mask, 0.125, causal, out_dtype=torch.float32)
+    o_ref, lse_ref = attn_fwd64_sparse(inp["q"], inp["k"], inp["v"], 0.125, causal, kv_len, mask.numpy())
+    check_fwd(o, lse, o_ref, lse_ref)
+    assert torch.all(o[:, :, 128:256] == 0) and torch.all(torch.isneginf(lse[:, :, 128:256]))
+    ref = attn_bwd64_sparse(inp["q"], inp["k"], inp["v"], inp["do"], 0.125, causal, kv_len, mask.numpy())
+    check_grads(grads, ref, "kv_len")
+    dq, dk, dv = grads
+    assert torch.all(dq[:, :, 128:256] == 0)
+    for b, L in enumerate(kv_len):
+        assert torch.all(dk[b, :, L:] == 0) and torch.all(dv[b, :, L:] == 0)
+
+
+def test_empty_mask_gives_zeros():
+    say("sparse empty mask")
+    inp = W.random_case(1, 2, 300, 64, "bf16", seed=8, backward=True)
+    mask = torch.zeros(3, 3, dtype=torch.uint8)
+    o, lse, grads = run(inp, mask, 0.125, False)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    for g in grads:
+        assert torch.all(g == 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_full_mask_is_plain_attention_bit_for_bit(d, causal):
+    B, H, N = 2, 2, 700
+    say(f"sparse all-kept vs plain d={d} causal={causal}")
+    inp = W.random_case(B, H, N, d, "bf16", seed=d + 3 * causal, causal=causal, backward=True)
+    nb = (N + 127) // 128
+    mask = torch.ones(nb, nb, dtype=torch.uint8)
+    if causal:
+        mask = torch.tril(mask)  # the blocks above the diagonal hold no visible key
+    o, lse, grads = run(inp, mask, d ** -0.5, causal)
+    q, k, v, do = (dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o2, lse2 = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    fa_fwd(q, k, v, o2, lse2, d ** -0.5, causal)
+    g2 = [torch.empty_like(q) for _ in range(3)]
+    fa_bwd(q, k, v, o2, do, lse2, *g2, d ** -0.5, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for a, b in zip(grads, g2):
+        assert torch.equal(a, b)
+
+
+def test_shared_mask_equals_per_head_copies():
+    B, H, N, d = 2, 3, 600, 64
+    say("sparse shared vs per-head mask")
+    inp = W.random_case(B, H, N, d, "fp16", seed=12, backward=True)
+    m2 = W.random_block_mask((), N, 0.5, seed=13)
+    a = run(inp, m2, 0.125, True)
+    b = run(inp, m2.expand(B, H, *m2.shape).contiguous(), 0.125, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        assert torch.equal(x, y)
+
+
+def test_measurement_shape_sampled_against_oracle():
+    """B=1 H=16 N=16384 d=64 bf16 with the band-and-first-block mask: O, LSE
+    on sampled rows of two heads; dQ on sampled rows and dK, dV on sampled
+    keys of one head."""
+    w = W.SPARSE
+    say(f"sparse full size {w.name}")
+    inp = W.make_inputs(w, seed=0)
+    mask = W.block_mask(w)
+    o, lse, grads = run(inp, mask, w.scale, w.causal, out_dtype=torch.float32)
+    rows = [0, 1, 127, 128, 129, 5000, 8191, 8192, 16000, w.N - 1]
+    for h in (0, w.H - 1):
+        o_ref, lse_ref = attn_fwd64_sparse(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1],
+                                           inp["v"][:, h:h + 1], w.scale, w.causal, None,
+                                           mask.numpy(), rows=rows)
+        st = fwd_stats(np64(o[:, h:h + 1, rows]), np64(lse[:, h:h + 1, rows]), o_ref, lse_ref)
+        assert st["max_abs"] <= FWD_MAX_ABS and st["lse_max_abs"] <= LSE_MAX_ABS, st
+    h = 5
+    sq, sk, sv = attn_bwd64_sparse_sampled(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.causal,
+                                           None, mask.numpy(), [(0, h)], rows, rows)
+    dq, dk, dv = grads
+    for name, got, ref in (("dq", dq[0, h, rows], sq[0]), ("dk", dk[0, h, rows], sk[0]),
+                           ("dv", dv[0, h, rows], sv[0])):
+        e = rel_fro(np64(got), ref)
+        print(f"full size {name} rel-fro {e:.2e}", flush=True)
+        assert e <= GRAD_REL_FRO, (name, e)

@@ -9,15 +9,17 @@
   * a block-diagonal mask is plain attention run on each block's slice of
     the sequence on its own;
   * an all-zero mask gives O = 0, LSE = -inf and zero gradients;
-  * the backward against central finite differences of the brute-force loss.
+  * the backward against central finite differences of the brute-force loss;
+  * the row subset of the forward and the sampled backward (for N too long
+    for an N x N matrix) against the whole, pinned computation.
 """
 import math
 
 import numpy as np
 import pytest
 
-from oracle import (attn_bwd64, attn_bwd64_sparse, attn_fwd64, attn_fwd64_sparse,
-                    brute_head_allowed, brute_loss_allowed)
+from oracle import (attn_bwd64, attn_bwd64_sparse, attn_bwd64_sparse_sampled, attn_fwd64,
+                    attn_fwd64_sparse, brute_head_allowed, brute_loss_allowed)
 
 
 def rnd(shape, seed):
@@ -137,3 +139,25 @@ def test_sparse_backward_matches_finite_differences(causal):
             lm = brute_loss_allowed(args_m["q"][0, 0], args_m["k"][0, 0], args_m["v"][0, 0], do[0, 0], 0.8, allowed)
             fd[idx] = (lp - lm) / (2 * step)
         np.testing.assert_allclose(g, fd, rtol=0, atol=1e-7, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_and_keys_match_the_whole_backward(causal):
+    B, H, N, d, blk = 2, 2, 37, 3, 4
+    q, k, v, do = (rnd((B, H, N, d), s) for s in range(60, 64))
+    nb = (N + blk - 1) // blk
+    mask = (np.random.default_rng(9).random((B, H, nb, nb)) < 0.5).astype(np.uint8)
+    kv = [37, 21]
+    rows = [0, 3, 4, 20, 21, 36]
+    o, lse = attn_fwd64_sparse(q, k, v, 0.6, causal, kv, mask, block=blk)
+    o_r, lse_r = attn_fwd64_sparse(q, k, v, 0.6, causal, kv, mask, block=blk, rows=rows, row_chunk=4)
+    np.testing.assert_allclose(o_r, o[:, :, rows], atol=1e-14)
+    np.testing.assert_array_equal(lse_r, lse[:, :, rows])
+    dq, dk, dv = attn_bwd64_sparse(q, k, v, do, 0.6, causal, kv, mask, block=blk)
+    heads = [(0, 1), (1, 0)]
+    sq, sk, sv = attn_bwd64_sparse_sampled(q, k, v, do, 0.6, causal, kv, mask, heads, rows, rows,
+                                           block=blk, row_chunk=5)
+    for t, (b, h) in enumerate(heads):
+        np.testing.assert_allclose(sq[t], dq[b, h, rows], atol=1e-12)
+        np.testing.assert_allclose(sk[t], dk[b, h, rows], atol=1e-12)
+        np.testing.assert_allclose(sv[t], dv[b, h, rows], atol=1e-12)
