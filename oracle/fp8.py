@@ -1,0 +1,185 @@
+"""FP8 attention forward with incoherent processing, step by step.
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package.
+
+The marketmaker.cc article (section "FA3：料斗力学", item 3) says that plain
+FP8 attention is spoiled by outliers and that the FP8 path of FlashAttention-3
+rotates the vectors at random before quantising them block by block, which
+spreads an outlier over all coordinates; the Ultralytics glossary page
+("FlashAttention-2, -3 e -4") adds that FlashAttention-3 supports FP8. The
+pages give no formulas. This is an approximation, so the oracle follows the
+steps of the method in order, with these readings:
+
+  * rotation: y = FWHT(x * s) for every row x of Q and of K, where s is a
+    random +-1 vector of length d (an input) and FWHT the unnormalised
+    Walsh-Hadamard transform, in fp32, stage by stage (h = 1, 2, ..., d/2;
+    elements i and i + h with bit h of i clear become a + b and a - b). The
+    rotation is orthogonal up to the factor d: (Q R)(K R)^T = d Q K^T, so the
+    scores carry an extra 1/d. V is not rotated;
+  * quantisation to OCP FP8 e4m3 (bias 7, max 448, no infinities), block by
+    block: one fp32 scale per block of 128 query rows, per block of 64 key
+    rows, and per head for V; scale = amax / 448 and code =
+    e4m3_rne(clamp(x * (448 / amax), -448, 448)), every product and quotient
+    in fp32 (the precision in which the codes are decided); an all-zero block
+    has scale 0 and codes 0;
+  * attention over the dequantised Q and K in fp64, tile by tile over 64
+    keys with the running row max and running sum of the online softmax
+    (marketmaker.cc article, section "在线softmax递归"); in each tile the
+    probabilities p = exp(S - m) (m the running max after the tile) are
+    quantised as e4m3_rne(256 p) before the P V product; the running sum adds
+    the unquantised p; the output is acc * scale_v / l and LSE = m + ln l.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _kv_lens
+
+__all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "fwht32", "fp8_quantize_rows",
+           "fp8_quantize", "attn_fwd64_fp8"]
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values (fp64) of OCP e4m3 codes: sign, 4-bit exponent (bias 7), 3-bit
+    mantissa; exponent 0 is subnormal (m * 2^-9); 0x7f / 0xff are NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round-to-nearest-even of each value to the e4m3 grid, as uint8 codes.
+    |x| must not exceed 448 (the caller clamps); -0 keeps its sign bit."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_encode: |x| > 448, clamp first")
+    sign = np.signbit(x).astype(np.int64) << 7
+    a = np.abs(x)
+    # subnormal range: steps of 2^-9 below 2^-6 (a step count of 8 is 2^-6,
+    # which is the code of the smallest normal number, so no special case)
+    sub = np.rint(a / 2.0 ** -9).astype(np.int64)
+    mant, ex = np.frexp(np.where(a > 0, a, 1.0))       # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex - 1                                          # a = (2 mant) * 2^e, 2 mant in [1, 2)
+    m = np.rint((2.0 * mant - 1.0) * 8.0).astype(np.int64)
+    e = np.where(m == 8, e + 1, e)
+    m = np.where(m == 8, 0, m)
+    norm = ((e + 7) << 3) | m
+    code = np.where(a < 2.0 ** -6, sub, norm)
+    return (sign | code).astype(np.uint8)
+
+
+def fwht32(x) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform of the last axis (a power of
+    two) in fp32, stage by stage: h = 1, 2, 4, ...; indices i and i + h with
+    bit h of i clear become (a + b, a - b)."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    d = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < d:
+        z = y.reshape(lead + (d // (2 * h), 2, h))
+        a = z[..., 0, :].copy()
+        b = z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(lead + (d,))
+        h *= 2
+    return y
+
+
+def fp8_quantize_rows(x32: np.ndarray, block: int):
+    """Quantise fp32 rows [..., N, d] in blocks of ``block`` rows (the last
+    block may be short). Returns (codes uint8 [..., N, d], scales fp32
+    [..., ceil(N / block)])."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    N = x32.shape[-2]
+    nb = (N + block - 1) // block
+    codes = np.zeros(x32.shape, dtype=np.uint8)
+    scales = np.zeros(x32.shape[:-2] + (nb,), dtype=np.float32)
+    for i in range(nb):
+        blk = x32[..., i * block:(i + 1) * block, :]
+        amax = np.abs(blk).max(axis=(-2, -1)).astype(np.float32)
+        safe = np.where(amax > 0, amax, np.float32(1))
+        inv = np.where(amax > 0, np.float32(E4M3_MAX) / safe, np.float32(0)).astype(np.float32)
+        scales[..., i] = np.where(amax > 0, safe / np.float32(E4M3_MAX), np.float32(0))
+        t = (blk * inv[..., None, None]).astype(np.float32)
+        t = np.clip(t, -np.float32(E4M3_MAX), np.float32(E4M3_MAX))
+        codes[..., i * block:(i + 1) * block, :] = e4m3_encode(t)
+    return codes, scales
+
+
+def _to32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to(device="cpu", dtype=torch.float32).numpy()
+    return np.asarray(x, dtype=np.float32)
+
+
+def fp8_quantize(q, k, v, signs=None, block_q: int = 128, block_k: int = 64):
+    """The quantisation step. q, k, v: [B, H, N, d] (any float type, exactly
+    widened to fp32); signs: +-1 vector of length d, or None for no rotation.
+    Returns a dict: q8, k8, v8 (uint8 [B, H, N, d], row-major), sq [B, H,
+    ceil(N / block_q)], sk [B, H, ceil(N / block_k)], sv [B, H] (fp32)."""
+    q32, k32, v32 = _to32(q), _to32(k), _to32(v)
+    if signs is not None:
+        s = np.asarray(signs, dtype=np.float32)
+        q32 = fwht32(q32 * s)
+        k32 = fwht32(k32 * s)
+    q8, sq = fp8_quantize_rows(q32, block_q)
+    k8, sk = fp8_quantize_rows(k32, block_k)
+    N = v32.shape[-2]
+    v8, sv = fp8_quantize_rows(v32, max(N, 1))
+    return {"q8": q8, "k8": k8, "v8": v8, "sq": sq, "sk": sk, "sv": sv[..., 0],
+            "rotated": signs is not None}
+
+
+def attn_fwd64_fp8(qz: dict, scale: float, causal: bool = False, kv_len=None, tile: int = 64,
+                   block_q: int = 128, block_k: int = 64, p_scale: float = 256.0,
+                   quantize_p: bool = True):
+    """Attention over the quantised inputs of ``fp8_quantize`` (tile by tile,
+    P quantised per tile; see the module text). ``quantize_p=False`` skips
+    the quantisation of P (for pinning the rest). Returns (O [B, H, N, d],
+    LSE [B, H, N]) in fp64."""
+    q8, k8, v8 = qz["q8"], qz["k8"], qz["v8"]
+    B, H, N, d = q8.shape
+    lens = _kv_lens(kv_len, B, N)
+    rows = np.arange(N)
+    s_mul = scale / (d if qz["rotated"] else 1)
+    o = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            qd = e4m3_decode(q8[b, h]) * np.repeat(qz["sq"][b, h].astype(np.float64), block_q)[:N, None]
+            kd = e4m3_decode(k8[b, h]) * np.repeat(qz["sk"][b, h].astype(np.float64), block_k)[:N, None]
+            vd = e4m3_decode(v8[b, h])
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            acc = np.zeros((N, d))
+            for t0 in range(0, N, tile):
+                cols = np.arange(t0, min(t0 + tile, N))
+                s = s_mul * (qd @ kd[cols].T)
+                vis = cols[None, :] < lens[b]
+                if causal:
+                    vis = vis & (cols[None, :] <= rows[:, None])
+                s = np.where(vis, s, -np.inf)
+                m_new = np.maximum(m, s.max(axis=1))
+                grow = m_new > m
+                alpha = np.where(grow, np.exp(np.where(grow, m - m_new, 0.0)), 1.0)
+                l *= alpha
+                acc *= alpha[:, None]
+                m_safe = np.where(np.isfinite(m_new), m_new, 0.0)
+                p = np.where(vis, np.exp(s - m_safe[:, None]), 0.0)
+                l += p.sum(axis=1)
+                pq = e4m3_decode(e4m3_encode(p * p_scale)) / p_scale if quantize_p else p
+                acc += pq @ vd[cols]
+                m = m_new
+            has = l > 0
+            o[b, h] = np.where(has[:, None], acc * float(qz["sv"][b, h]) / np.where(has, l, 1.0)[:, None], 0.0)
+            lse[b, h] = np.where(has, m + np.log(np.where(has, l, 1.0)), -np.inf)
+    return o, lse
