@@ -35,6 +35,7 @@ METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak on 1x MI355X"
 # MI355X dense peaks: bf16/fp16 MFMA 256 CU x 4096 FLOP/clk x 2.4 GHz, HBM3E 8 TB/s.
 PEAK_BF16_FLOPS = 256 * 4096 * 2.4e9
 PEAK_HBM_BYTES = 8.0e12
+PEAK_FP8_FLOPS = 256 * 8192 * 2.4e9  # dense FP8 matrix-core rate, twice bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # roofline bound of each kernel of the step
@@ -237,7 +238,47 @@ def run_gpu(args):
         out["extra"][W.FEW_HEADS.name] = split_config(torch, W)
         out["extra"][W.GQA.name] = gqa_config(torch, W)
         out["extra"][W.SPARSE.name] = sparse_config(torch, W)
+        out["extra"][W.FP8.name] = fp8_config(torch, W)
     return out
+
+
+def fp8_config(torch, W):
+    """The FP8 forward with incoherent processing on the outlier-channel
+    workload: the quantisation launches (HBM-bound) and the attention kernel
+    timed apart and together, against the bf16 forward on the same inputs.
+    FLOPs are the forward's 4 d N^2 per head (x 1/2 causal)."""
+    from exact_io_aware_07_amd import (fa_fp8_quantize, fa_fwd, fa_fwd_fp8, fa_fwd_fp8_incoherent,
+                                       fa_fwd_fp8_workspace_bytes, fp8_buffers)
+    w = W.FP8
+    inp = W.make_inputs(w)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    signs = W.random_signs(w.d, seed=0).cuda()
+    bufs = fp8_buffers(w.B, w.H, w.N, w.d)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa_fwd_fp8_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+    fa_fp8_quantize(q, k, v, signs, bufs)
+    flops = fwd_flops(w)
+    runs = {
+        "quantize": lambda: fa_fp8_quantize(q, k, v, signs, bufs),
+        "attention_fp8": lambda: fa_fwd_fp8(bufs, True, o, lse, w.scale, w.causal),
+        "fp8_total": lambda: fa_fwd_fp8_incoherent(q, k, v, signs, o, lse, w.scale, w.causal, None, ws),
+        "bf16_fwd": lambda: fa_fwd(q, k, v, o, lse, w.scale, w.causal),
+    }
+    entry = {}
+    for name, fn in runs.items():
+        entry[f"{name}_ms"] = median_ms(torch, fn)
+    # compulsory bytes of the quantisation: Q, K, V read once (2 bytes each),
+    # the three code arrays written (1 byte each); V is in fact read twice
+    qbytes = 9 * w.B * w.H * w.N * w.d
+    entry["quantize_gbps_compulsory"] = qbytes / (entry["quantize_ms"] * 1e-3) / 1e9
+    for name in ("attention_fp8", "fp8_total", "bf16_fwd"):
+        rate = flops / (entry[f"{name}_ms"] * 1e-3)
+        entry[f"{name}_tflops"] = rate / 1e12
+    entry["attention_fp8_pct_of_fp8_peak"] = 100 * entry["attention_fp8_tflops"] * 1e12 / PEAK_FP8_FLOPS
+    entry["speedup_total_vs_bf16"] = entry["bf16_fwd_ms"] / entry["fp8_total_ms"]
+    log(f"[bench] extra {w.name}: {entry}")
+    return entry
 
 
 def median_ms(torch, fn, iters: int = 10) -> float:

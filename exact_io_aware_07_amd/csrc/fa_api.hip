@@ -78,6 +78,25 @@ size_t gqa_part_bytes(int B, int Hkv, int N, int d, int gsplit) {
   return 2 * (size_t)gsplit * B * Hkv * N * (size_t)d * sizeof(float);
 }
 
+// FP8 path: element counts of its buffers and the layout of the workspace
+// of fa_fwd_fp8_incoherent (regions in this order, each at a multiple of
+// 256 bytes).
+struct Fp8Sizes {
+  size_t qk, vt, nq, nk, bh;  // codes of Q (and of K), of V^T; scale counts
+  int Np;
+};
+Fp8Sizes fp8_sizes(int B, int H, int N, int d) {
+  Fp8Sizes z;
+  z.bh = (size_t)B * H;
+  z.Np = ((N + 63) / 64) * 64;
+  z.qk = z.bh * N * d;
+  z.vt = z.bh * d * z.Np;
+  z.nq = z.bh * ((N + 127) / 128);
+  z.nk = z.bh * ((N + 63) / 64);
+  return z;
+}
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 // Positions of a partial step are bounded so that every sum of a position
 // difference and a row index stays inside a 32-bit int.
 constexpr int kMaxPos = 1 << 29;
@@ -372,6 +391,84 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
                     scale, causal, stream, dtype,
                     (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV, H, 1, nullptr, block_mask,
                     mask_stride_b, mask_stride_h);
+}
+
+int fa_fp8_quantize(const void* q, const void* k, const void* v, const signed char* signs,
+                    unsigned char* q8, unsigned char* k8, unsigned char* vt8, float* q_scale,
+                    float* k_scale, float* v_scale, float* v_amax, int B, int H, int N, int d,
+                    void* stream, int in_dtype) {
+  int st = check_scalars(B, H, N, d, 1.f, 0);
+  if (st != FA_OK) return st;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !q8 || !k8 || !vt8 || !q_scale || !k_scale || !v_scale || !v_amax)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) ||
+      !aligned16(vt8) || !aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale) ||
+      !aligned4(v_amax))
+    return FA_ERR_INVALID_ARG;
+  fa::Fp8QuantArgs a{q, k, v, signs, q8, k8, vt8, q_scale, k_scale, v_scale, v_amax,
+                     B, H, N, d, fp8_sizes(B, H, N, d).Np};
+  hipError_t e = fa::launch_fp8_quantize(a, elem(in_dtype), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const unsigned char* vt8,
+               const float* q_scale, const float* k_scale, const float* v_scale, int rotated,
+               void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+               const int* kv_len, void* stream, int o_dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (!dtype_ok(o_dtype)) return FA_ERR_UNSUPPORTED;
+  if (rotated != 0 && rotated != 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q8 || !k8 || !vt8 || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(vt8) || !aligned4(q_scale) ||
+      !aligned4(k_scale) || !aligned4(v_scale) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  fa::Fp8FwdArgs a{q8, k8, vt8, q_scale, k_scale, v_scale, o, lse, kv_len, B, H, N, d,
+                   fp8_sizes(B, H, N, d).Np, scale, causal, rotated, o_dtype == FA_BF16 ? 1 : 0};
+  hipError_t e = fa::launch_fwd_fp8(a, elem(o_dtype), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 0;
+  const Fp8Sizes z = fp8_sizes(B, H, N, d);
+  return 2 * up256(z.qk) + up256(z.vt) + up256(z.nq * 4) + up256(z.nk * 4) + up256(z.bh * 4) +
+         up256(z.nk * 4);
+}
+
+int fa_fwd_fp8_incoherent(const void* q, const void* k, const void* v, const signed char* signs,
+                          void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+                          const int* kv_len, void* workspace, size_t workspace_bytes, void* stream,
+                          int in_dtype, int o_dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < fa_fwd_fp8_workspace_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  const Fp8Sizes z = fp8_sizes(B, H, N, d);
+  unsigned char* w = (unsigned char*)workspace;
+  unsigned char* q8 = w;
+  unsigned char* k8 = q8 + up256(z.qk);
+  unsigned char* vt8 = k8 + up256(z.qk);
+  float* qs = (float*)(vt8 + up256(z.vt));
+  float* ks = (float*)((unsigned char*)qs + up256(z.nq * 4));
+  float* vs = (float*)((unsigned char*)ks + up256(z.nk * 4));
+  float* va = (float*)((unsigned char*)vs + up256(z.bh * 4));
+  st = fa_fp8_quantize(q, k, v, signs, q8, k8, vt8, qs, ks, vs, va, B, H, N, d, stream, in_dtype);
+  if (st != FA_OK) return st;
+  return fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, signs ? 1 : 0, o, lse, B, H, N, d, scale, causal,
+                    kv_len, stream, o_dtype);
 }
 
 const char* fa_strerror(int status) {

@@ -98,6 +98,44 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, Elem t, int stages, hipStream_t s);
 hipError_t launch_bwd_mfma_sparse(const BwdArgs& a, Elem t, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
 
+// FP8 forward with incoherent processing. Quantisation: Q and K rows
+// rotated (sign flip by `signs`, unless NULL, then the unnormalised
+// Walsh-Hadamard transform) and quantised to e4m3 per block (128 / 64
+// rows); V per head, written transposed [B, H, d, Np] (Np = N rounded up to
+// 64, zero codes past N). v_amax: [B, H, ceil(N / 64)] scratch.
+struct Fp8QuantArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const signed char* signs;
+  unsigned char* q8;
+  unsigned char* k8;
+  unsigned char* vt8;
+  float* q_scale;  // [B, H, ceil(N / 128)]
+  float* k_scale;  // [B, H, ceil(N / 64)]
+  float* v_scale;  // [B, H]
+  float* v_amax;
+  int B, H, N, d, Np;
+};
+struct Fp8FwdArgs {
+  const unsigned char* q8;
+  const unsigned char* k8;
+  const unsigned char* vt8;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  void* o;
+  float* lse;
+  const int* kv_len;
+  int B, H, N, d, Np;
+  float scale;
+  int causal;
+  int rotated;  // scores carry the extra 1/d of the unnormalised rotation
+  int o_bf16;   // 16-bit output: bf16 (1) or fp16 (0)
+};
+hipError_t launch_fp8_quantize(const Fp8QuantArgs& a, Elem in, hipStream_t s);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, Elem out, hipStream_t s);
+
 // Merge of partial results (fp32 O [rows][d] and LSE [rows] per part) into
 // out_o (fp32, fp16 or bf16) and out_lse. out_o / out_lse may alias part 0
 // when the output is fp32.

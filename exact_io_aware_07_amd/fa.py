@@ -21,7 +21,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0,
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_dsum", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_partial", "fa_merge", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split", "fa_fwd_gqa", "fa_bwd_gqa_workspace_bytes", "fa_bwd_gqa",
-           "fa_fwd_sparse", "fa_bwd_sparse", "fa_strerror")
+           "fa_fwd_sparse", "fa_bwd_sparse", "fa_fp8_quantize", "fa_fwd_fp8",
+           "fa_fwd_fp8_workspace_bytes", "fa_fwd_fp8_incoherent", "fa_strerror")
 
 _DTYPE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib: Optional[ctypes.CDLL] = None
@@ -75,6 +76,14 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, ll,
                                 ll, vp, sz, vp, i]
     L.fa_bwd_sparse.restype = i
+    L.fa_fp8_quantize.argtypes = [vp] * 11 + [i, i, i, i, vp, i]
+    L.fa_fp8_quantize.restype = i
+    L.fa_fwd_fp8.argtypes = [vp] * 6 + [i, vp, vp, i, i, i, i, f, i, vp, vp, i]
+    L.fa_fwd_fp8.restype = i
+    L.fa_fwd_fp8_workspace_bytes.argtypes = [i, i, i, i]
+    L.fa_fwd_fp8_workspace_bytes.restype = sz
+    L.fa_fwd_fp8_incoherent.argtypes = [vp] * 6 + [i, i, i, i, f, i, vp, vp, sz, vp, i, i]
+    L.fa_fwd_fp8_incoherent.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -386,6 +395,86 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, block_mask, scale: float,
                              _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_sparse")
+
+
+def fp8_buffers(B: int, H: int, N: int, d: int, device="cuda") -> dict:
+    """Device buffers for fa_fp8_quantize / fa_fwd_fp8 (allocated with torch)."""
+    np_ = (N + 63) // 64 * 64
+    u8, f32 = torch.uint8, torch.float32
+    return {"q8": torch.empty((B, H, N, d), dtype=u8, device=device),
+            "k8": torch.empty((B, H, N, d), dtype=u8, device=device),
+            "vt8": torch.empty((B, H, d, np_), dtype=u8, device=device),
+            "q_scale": torch.empty((B, H, (N + 127) // 128), dtype=f32, device=device),
+            "k_scale": torch.empty((B, H, (N + 63) // 64), dtype=f32, device=device),
+            "v_scale": torch.empty((B, H), dtype=f32, device=device),
+            "v_amax": torch.empty((B, H, (N + 63) // 64), dtype=f32, device=device)}
+
+
+def _signs(signs, d):
+    if signs is None:
+        return None
+    _check_tensor("signs", signs, (d,), torch.int8)
+    return signs.data_ptr()
+
+
+def fa_fp8_quantize(q, k, v, signs, bufs: dict, stream=None) -> None:
+    """Enqueue the rotation (signs: int8 [d] of +-1, or None) and e4m3
+    quantisation of q, k, v [B, H, N, d] into ``bufs`` (see fp8_buffers)."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    ref = fp8_buffers(B, H, N, d, device="meta")
+    for name, t in bufs.items():
+        _check_tensor(name, t, ref[name].shape, ref[name].dtype)
+    st = lib().fa_fp8_quantize(_ptr(q), _ptr(k), _ptr(v), _signs(signs, d), _ptr(bufs["q8"]),
+                               _ptr(bufs["k8"]), _ptr(bufs["vt8"]), _ptr(bufs["q_scale"]),
+                               _ptr(bufs["k_scale"]), _ptr(bufs["v_scale"]), _ptr(bufs["v_amax"]),
+                               B, H, N, d, _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fp8_quantize")
+
+
+def fa_fwd_fp8(bufs: dict, rotated: bool, o, lse, scale: float, causal: bool = False,
+               kv_len=None, stream=None) -> None:
+    """Enqueue attention on the codes in ``bufs``: o [B, H, N, d] (fp32, fp16
+    or bf16), lse fp32 [B, H, N]."""
+    B, H, N, d = bufs["q8"].shape
+    _check_tensor("o", o, (B, H, N, d))
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    st = lib().fa_fwd_fp8(_ptr(bufs["q8"]), _ptr(bufs["k8"]), _ptr(bufs["vt8"]),
+                          _ptr(bufs["q_scale"]), _ptr(bufs["k_scale"]), _ptr(bufs["v_scale"]),
+                          int(bool(rotated)), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                          int(bool(causal)), _kv(kv_len, B), _stream(stream, o.device),
+                          _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+
+
+def fa_fwd_fp8_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().fa_fwd_fp8_workspace_bytes(B, H, N, d))
+
+
+def fa_fwd_fp8_incoherent(q, k, v, signs, o, lse, scale: float, causal: bool = False,
+                          kv_len=None, workspace=None, stream=None) -> None:
+    """Enqueue both FP8 steps (workspace allocated here when None)."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("o", o, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    need = fa_fwd_fp8_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_fwd_fp8_incoherent(_ptr(q), _ptr(k), _ptr(v), _signs(signs, d), _ptr(o),
+                                     _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+                                     _kv(kv_len, B), _ptr(workspace), ws_bytes,
+                                     _stream(stream, q.device), _DTYPE.get(q.dtype, -99),
+                                     _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8_incoherent")
 
 
 # Convenience wrappers that allocate the outputs with torch (plumbing only).

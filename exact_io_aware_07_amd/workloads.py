@@ -12,7 +12,9 @@ Recipe (applies to every workload):
   * then the per-workload extras, in this order: the key-padding lengths
     (``randint(lo, hi + 1, (B,))``), then the outlier key rows (for each
     (b, h) in row-major order, ``randperm(N)[:round(frac * N)]`` and those K
-    rows multiplied by the factor);
+    rows multiplied by the factor), then the outlier channels (for each
+    (b, h), ``randperm(d)[:count]`` and those columns of Q and K multiplied
+    by the factor);
   * finally a round-to-nearest-even cast of Q, K, V, dO to the workload dtype.
 
 The workloads are named after the shapes the pages discuss: BERT-large at
@@ -51,6 +53,8 @@ class Workload:
     measurement_only: bool = False
     Hkv: Optional[int] = None  # K/V heads (grouped-query attention); None means H
     block_pattern: Optional[str] = None  # block-sparse mask (see block_mask); None means dense
+    ch_outliers: int = 0               # channels of Q and K scaled per (b, h), FP8 workload
+    ch_outlier_scale: float = 1.0
     note: str = field(default="", compare=False)
 
     @property
@@ -115,8 +119,16 @@ SPARSE = Workload("long_block_sparse_band_bf16_fwd_bwd", 1, 16, 16384, 64, "bf16
                   backward=True, measurement_only=True, block_pattern="band_sink",
                   note="B=1 H=16 N=16384 d=64 bf16, 128x128 block mask: band of 3 + first block")
 
+# FP8 forward: the long-context shape with four outlier channels of Q and K
+# (x16, the same channels in Q and K of a head), the case the rotation of
+# the FP8 path is for.
+FP8 = Workload("long_context_fp8_outlier_channels_fwd", 1, 32, 4096, 128, "bf16",
+               measurement_only=True, ch_outliers=4, ch_outlier_scale=16.0,
+               note="B=1 H=32 N=4096 d=128 bf16, 4 channels of Q and K x16; FP8 forward")
+
 CONFIGS: Dict[str, Workload] = {w.name: w for w in (TINY, BERT, LONG, TRADE, GPT2)}
-MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD, FEW_HEADS, GQA, SPARSE)}
+MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD, FEW_HEADS, GQA, SPARSE,
+                                                        FP8)}
 ALL: Dict[str, Workload] = {**CONFIGS, **MEASUREMENT}
 
 
@@ -146,6 +158,13 @@ def make_inputs(w: Workload, seed: int = 0) -> Dict[str, Optional[torch.Tensor]]
             for h in range(w.kv_heads):
                 idx = torch.randperm(w.N, generator=g)[:count]
                 k[b, h, idx] *= w.k_outlier_scale
+    if w.ch_outliers > 0:
+        for b in range(w.B):
+            for h in range(w.H):
+                ch = torch.randperm(w.d, generator=g)[:w.ch_outliers]
+                q[b, h][:, ch] *= w.ch_outlier_scale
+                if h < w.kv_heads:
+                    k[b, h][:, ch] *= w.ch_outlier_scale
     dt = w.torch_dtype
     out = {
         "q": q.to(dt).contiguous(),
@@ -215,3 +234,10 @@ def random_block_mask(lead: Tuple[int, ...], N: int, keep: float, seed: int) -> 
     nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
     g = torch.Generator(device="cpu").manual_seed(seed)
     return (torch.rand(tuple(lead) + (nb, nb), generator=g) < keep).to(torch.uint8)
+
+
+def random_signs(d: int, seed: int) -> torch.Tensor:
+    """The +-1 vector (int8 [d]) of the FP8 path's rotation: one seeded
+    ``torch.randint(0, 2, (d,))`` draw mapped to -1 / +1."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (torch.randint(0, 2, (d,), generator=g) * 2 - 1).to(torch.int8)

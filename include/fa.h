@@ -242,6 +242,57 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o,
                   long long mask_stride_b, long long mask_stride_h, void* workspace,
                   size_t workspace_bytes, void* stream, int dtype);
 
+/*
+ * FP8 forward with incoherent processing (marketmaker.cc article, section
+ * "FA3：料斗力学", item 3: FP8 attention is spoiled by outliers, so the
+ * vectors are rotated at random before a block-wise quantisation, which
+ * spreads an outlier over all coordinates). An approximation of the
+ * attention above; two steps:
+ *
+ * fa_fp8_quantize: every row of q and k is multiplied elementwise by
+ * signs (device int8 [d], entries +1 or -1; NULL = no rotation) and put
+ * through the unnormalised Walsh-Hadamard transform in fp32, then
+ * quantised to OCP FP8 e4m3 (bias 7, largest 448): one fp32 scale per block
+ * of 128 query rows (q_scale [B,H,ceil(N/128)]) and of 64 key rows
+ * (k_scale [B,H,ceil(N/64)]), scale = amax / 448, code = round-to-nearest-
+ * even of clamp(x * (448 / amax), -448, 448) (all in fp32; an all-zero
+ * block has scale 0 and zero codes). V is not rotated: one scale per head
+ * (v_scale [B,H]), codes stored transposed in vt8 [B,H,d,Np], Np = N
+ * rounded up to 64, zero codes in the padding. q8, k8: [B,H,N,d] codes.
+ * v_amax: device scratch of B*H*ceil(N/64) floats. q, k, v fp16/bf16.
+ *
+ * fa_fwd_fp8: attention on those codes, S and P V on the FP8 matrix cores
+ * with fp32 accumulation, online softmax in fp32; P is quantised to e4m3
+ * as 256 p per 64-key tile against the running row max, the running sum
+ * adds the unquantised p. rotated (0 or 1) says whether the codes come
+ * from a rotation (the scores then carry 1/d, the rotation's factor).
+ * Writes o [B,H,N,d] in o_dtype (FA_F32, FA_F16, FA_BF16) and lse [B,H,N]
+ * as fa_fwd does; scale, causal and kv_len as for fa_fwd.
+ *
+ * fa_fwd_fp8_incoherent: both steps on one stream with the codes and
+ * scales in a caller-owned workspace of fa_fwd_fp8_workspace_bytes() bytes
+ * (16-byte aligned, contents on entry ignored); o_dtype is in_dtype or
+ * FA_F32. signs NULL runs the same path without the rotation.
+ * Errors as for fa_fwd; code buffers 16-byte aligned, scales 4-byte.
+ */
+int fa_fp8_quantize(const void* q, const void* k, const void* v,
+                    const signed char* signs, unsigned char* q8,
+                    unsigned char* k8, unsigned char* vt8, float* q_scale,
+                    float* k_scale, float* v_scale, float* v_amax, int B,
+                    int H, int N, int d, void* stream, int in_dtype);
+int fa_fwd_fp8(const unsigned char* q8, const unsigned char* k8,
+               const unsigned char* vt8, const float* q_scale,
+               const float* k_scale, const float* v_scale, int rotated,
+               void* o, float* lse, int B, int H, int N, int d, float scale,
+               int causal, const int* kv_len, void* stream, int o_dtype);
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N, int d);
+int fa_fwd_fp8_incoherent(const void* q, const void* k, const void* v,
+                          const signed char* signs, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int causal,
+                          const int* kv_len, void* workspace,
+                          size_t workspace_bytes, void* stream, int in_dtype,
+                          int o_dtype);
+
 /* Static, human-readable text for a status code. Never NULL. */
 const char* fa_strerror(int status);
 

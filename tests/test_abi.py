@@ -19,7 +19,7 @@ A = 0x100000  # a 16-byte aligned stand-in address: never dereferenced on these 
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_exported_entry_points():
@@ -347,3 +347,35 @@ def test_sparse_empty_calls_need_no_pointers():
                            None, fa.FA_BF16, fa.FA_BF16) == fa.FA_OK
     assert L.fa_bwd_sparse(None, None, None, None, None, None, None, None, None, 1, 2, 0, 64, 0.125,
                            0, None, None, 0, 0, None, 0, None, fa.FA_BF16) == fa.FA_OK
+
+
+def test_fp8_validation():
+    L = fa.lib()
+    q = lambda **kw: L.fa_fp8_quantize(*([A] * 11), kw.get("B", 1), 2, 300, kw.get("d", 64), None,
+                                       kw.get("it", fa.FA_BF16))
+    assert q(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert q(it=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert q(B=-1) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_fp8_quantize(*([A] * 3), None, None, *([A] * 6), 1, 2, 300, 64, None,
+                             fa.FA_BF16) == fa.FA_ERR_INVALID_ARG  # q8 missing
+    f = lambda **kw: L.fa_fwd_fp8(*([A] * 6), kw.get("rot", 1), A, A, 1, 2, 300, kw.get("d", 64),
+                                  kw.get("scale", 0.125), 0, None, None, kw.get("ot", fa.FA_BF16))
+    assert f(rot=2) == fa.FA_ERR_INVALID_ARG
+    assert f(scale=0.0) == fa.FA_ERR_INVALID_ARG
+    assert f(ot=9) == fa.FA_ERR_UNSUPPORTED
+    assert f(d=32) == fa.FA_ERR_UNSUPPORTED
+    w = lambda **kw: L.fa_fwd_fp8_incoherent(*([A] * 4), A, A, 1, 2, 300, 64, 0.125, 0, None,
+                                             kw.get("ws", A), kw.get("wb", 1 << 30), None,
+                                             kw.get("it", fa.FA_BF16), kw.get("ot", fa.FA_BF16))
+    assert w(ws=None) == fa.FA_ERR_WORKSPACE
+    assert w(wb=fa.fa_fwd_fp8_workspace_bytes(1, 2, 300, 64) - 1) == fa.FA_ERR_WORKSPACE
+    assert w(it=fa.FA_BF16, ot=fa.FA_F16) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_fp8_workspace_bytes(1, 2, 300, 96) == 0
+
+
+def test_fp8_workspace_holds_every_buffer():
+    B, H, N, d = 2, 3, 300, 128
+    np_ = 320
+    need = 2 * B * H * N * d + B * H * d * np_ + 4 * (B * H * 3 + 2 * B * H * 5 + B * H)
+    got = fa.fa_fwd_fp8_workspace_bytes(B, H, N, d)
+    assert need <= got <= need + 7 * 256
