@@ -533,15 +533,31 @@ def profile_workload(name: str, iters: int) -> None:
     from exact_io_aware_07_amd import attention_backward, attention_forward, lib
     from exact_io_aware_07_amd import workloads as W
     lib()
+    from exact_io_aware_07_amd import fa_bwd_sparse, fa_fwd_fp8_incoherent, fa_fwd_sparse
     w = W.ALL[name]
     inp = {n: (t.cuda() if t is not None else None) for n, t in W.make_inputs(w).items()}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     fwd_ms, bwd_ms = [], []
+    mask = W.block_mask(w)
+    mask = None if mask is None else mask.cuda()
+    signs = W.random_signs(w.d, seed=0).cuda() if w.ch_outliers else None
     for _ in range(iters):
         ev[0].record()
-        o, lse = attention_forward(inp["q"], inp["k"], inp["v"], w.causal, inp["kv_len"], w.scale)
+        if mask is not None:      # block-sparse
+            o = torch.empty_like(inp["q"])
+            lse = torch.empty(inp["q"].shape[:3], dtype=torch.float32, device="cuda")
+            fa_fwd_sparse(inp["q"], inp["k"], inp["v"], o, lse, mask, w.scale, w.causal)
+        elif signs is not None:   # FP8 with the rotation
+            o = torch.empty_like(inp["q"])
+            lse = torch.empty(inp["q"].shape[:3], dtype=torch.float32, device="cuda")
+            fa_fwd_fp8_incoherent(inp["q"], inp["k"], inp["v"], signs, o, lse, w.scale, w.causal)
+        else:
+            o, lse = attention_forward(inp["q"], inp["k"], inp["v"], w.causal, inp["kv_len"], w.scale)
         ev[1].record()
-        if w.backward:
+        if w.backward and mask is not None:
+            g = [torch.empty_like(inp["q"]) for _ in range(3)]
+            fa_bwd_sparse(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, *g, mask, w.scale, w.causal)
+        elif w.backward:
             attention_backward(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, w.causal,
                                inp["kv_len"], w.scale)
         ev[2].record()

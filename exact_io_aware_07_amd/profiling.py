@@ -37,6 +37,11 @@ KERNELS = {
     "dsum": ("dsum_kernel", "fa_bwd_mfma.hip"),
     "dkdv": ("dkdv_kernel", "fa_bwd_mfma.hip"),
     "dq": ("dq_kernel", "fa_bwd_mfma.hip"),
+    "dkv_reduce": ("dkv_reduce_kernel", "fa_bwd_mfma.hip"),
+    "merge": ("merge_kernel", "fa_merge.hip"),
+    "fp8_attn": ("fwd_fp8_kernel", "fa_fp8.hip"),
+    "fp8_qk": ("fp8_qk_kernel", "fa_fp8.hip"),
+    "fp8_v": ("fp8_v_kernel", "fa_fp8.hip"),
 }
 
 
