@@ -305,7 +305,9 @@ def sparse_config(torch, W):
     backward through fa_fwd_sparse / fa_bwd_sparse, TFLOP/s counted on the
     kept (query, key) pairs only, and the dense entry points on the same
     inputs for the speed-up (ideal: 1 / kept fraction)."""
-    from exact_io_aware_07_amd import fa_bwd, fa_bwd_sparse, fa_fwd, fa_fwd_sparse
+    from exact_io_aware_07_amd import (fa_bwd, fa_bwd_sparse, fa_bwd_sparse_planned,
+                                       fa_bwd_sparse_planned_workspace_bytes, fa_fwd, fa_fwd_sparse,
+                                       fa_sparse_bwd_plan)
     w = W.SPARSE
     inp = W.make_inputs(w)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
@@ -318,10 +320,16 @@ def sparse_config(torch, W):
     kept = float(mask.sum().item()) * W.MASK_BLOCK * W.MASK_BLOCK * w.B * w.H
     fwd_kept = 4.0 * w.d * kept
     fa_fwd_sparse(q, k, v, o, lse, mask, w.scale, w.causal)
+    plan = fa_sparse_bwd_plan(W.block_mask(w), w.B, w.H, w.N, w.causal)
+    plan = {"items": plan["items"].cuda(), "cols": plan["cols"].cuda(), "n_slots": plan["n_slots"]}
+    ws_p = torch.empty(fa_bwd_sparse_planned_workspace_bytes(w.B, w.H, w.N, w.d, plan["n_slots"]),
+                       dtype=torch.uint8, device="cuda")
     runs = {
         "fwd_sparse": (lambda: fa_fwd_sparse(q, k, v, o, lse, mask, w.scale, w.causal), 1.0),
         "bwd_sparse": (lambda: fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, mask, w.scale,
                                              w.causal, None, ws), 2.5),
+        "bwd_sparse_planned": (lambda: fa_bwd_sparse_planned(q, k, v, o, do, lse, dq, dk, dv, mask, plan,
+                                                             w.scale, w.causal, None, ws_p), 2.5),
     }
     entry = {"kept_fraction": kept / (w.B * w.H * w.N * w.N), "mask": w.block_pattern}
     for name, (fn, mult) in runs.items():
@@ -339,6 +347,7 @@ def sparse_config(torch, W):
         entry[name] = median_ms(torch, fn)
     entry["fwd_speedup_vs_dense"] = entry["fwd_dense_ms"] / entry["fwd_sparse_ms"]
     entry["bwd_speedup_vs_dense"] = entry["bwd_dense_ms"] / entry["bwd_sparse_ms"]
+    entry["bwd_planned_speedup_vs_dense"] = entry["bwd_dense_ms"] / entry["bwd_sparse_planned_ms"]
     log(f"[bench] extra {w.name}: {entry}")
     return entry
 

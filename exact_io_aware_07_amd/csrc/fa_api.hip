@@ -3,6 +3,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "fa.h"
 #include "fa_internal.h"
 
@@ -391,6 +394,101 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
                     scale, causal, stream, dtype,
                     (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV, H, 1, nullptr, block_mask,
                     mask_stride_b, mask_stride_h);
+}
+
+int fa_sparse_bwd_plan(const unsigned char* host_mask, long long mask_stride_b,
+                       long long mask_stride_h, int B, int H, int N, int causal, int* items,
+                       int max_items, int* cols, int max_cols, int* n_items, int* n_cols,
+                       int* n_slots) {
+  if (B < 0 || H < 0 || N < 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+  if (mask_stride_b < 0 || mask_stride_h < 0 || !n_items || !n_cols || !n_slots)
+    return FA_ERR_INVALID_ARG;
+  const int nb = (N + fa::kMaskBlock - 1) / fa::kMaskBlock;
+  if (nb > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N > 0 && !host_mask) return FA_ERR_INVALID_ARG;
+  struct Item { int bh, kb, first, slot, size; };
+  std::vector<Item> its;
+  std::vector<int> cs;
+  int slots = 0;
+  const int C = fa::kSparsePiece;
+  for (int b = 0; b < B && N > 0; ++b) {
+    for (int h = 0; h < H; ++h) {
+      const unsigned char* m = host_mask + b * mask_stride_b + h * mask_stride_h;
+      for (int kb = 0; kb < nb; ++kb) {
+        int n = 0;
+        for (int qb = causal ? kb : 0; qb < nb; ++qb) n += m[(long long)qb * nb + kb] != 0;
+        const int bh = b * H + h;
+        if (n <= C) {
+          its.push_back({bh, kb, 0, -1, n});
+          continue;
+        }
+        const int pieces = (n + C - 1) / C;
+        for (int i = 0; i < pieces; ++i) its.push_back({bh, kb, i * C, slots + i, std::min(C, n - i * C)});
+        cs.insert(cs.end(), {bh, kb, slots, pieces});
+        slots += pieces;
+      }
+    }
+  }
+  // longest pieces first, so that they do not start last
+  std::stable_sort(its.begin(), its.end(), [](const Item& x, const Item& y) { return x.size > y.size; });
+  *n_items = (int)its.size();
+  *n_cols = (int)cs.size() / 4;
+  *n_slots = slots;
+  if (!items && !cols) return FA_OK;  // counts only
+  if (!items || !cols || max_items < *n_items || max_cols < *n_cols) return FA_ERR_INVALID_ARG;
+  for (size_t i = 0; i < its.size(); ++i) {
+    items[4 * i] = its[i].bh;
+    items[4 * i + 1] = its[i].kb;
+    items[4 * i + 2] = its[i].first;
+    items[4 * i + 3] = its[i].slot;
+  }
+  std::copy(cs.begin(), cs.end(), cols);
+  return FA_OK;
+}
+
+size_t fa_bwd_sparse_planned_workspace_bytes(int B, int H, int N, int d, int n_slots) {
+  if (B < 0 || H < 0 || N < 0 || n_slots < 0 || (d != 64 && d != 128)) return 0;
+  return dsum_bytes_aligned(B, H, N) +
+         2 * (size_t)n_slots * fa::kMaskBlock * (size_t)d * sizeof(float);
+}
+
+int fa_bwd_sparse_planned(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                          int H, int N, int d, float scale, int causal, const int* kv_len,
+                          const unsigned char* block_mask, long long mask_stride_b,
+                          long long mask_stride_h, const int* items, int n_items,
+                          const int* cols, int n_cols, int n_slots, void* workspace,
+                          size_t workspace_bytes, void* stream, int dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if ((N + fa::kMaskBlock - 1) / fa::kMaskBlock > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
+  if (n_items < 0 || n_cols < 0 || n_slots < 0 || (n_cols > 0) != (n_slots > 0))
+    return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N == 0) return FA_OK;
+  // every key block of every head has at least one item
+  if ((long long)n_items < (long long)B * H * ((N + fa::kMaskBlock - 1) / fa::kMaskBlock))
+    return FA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !block_mask || !items)
+    return FA_ERR_INVALID_ARG;
+  if (n_cols > 0 && !cols) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse) || !aligned4(items) ||
+      (cols && !aligned4(cols)))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, n_slots))
+    return FA_ERR_WORKSPACE;
+  float* part = (float*)((char*)workspace + dsum_bytes_aligned(B, H, N));
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d, scale,
+                causal, H, 1, part, block_mask, mask_stride_b, mask_stride_h, items, cols,
+                n_items, n_cols, n_slots};
+  hipError_t e = fa::launch_bwd_mfma_sparse(a, elem(dtype),
+                                            (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int fa_fp8_quantize(const void* q, const void* k, const void* v, const signed char* signs,

@@ -126,9 +126,19 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   const int S = a.gsplit;
   const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nkb, a.B * a.Hkv * S, a.causal,
                                   DkdvCfg<D>::MINW);
-  const int bhk = pk.bh / S;  // K/V head
+  int bhk = pk.bh / S;  // K/V head
   const int share = pk.bh - bhk * S;
-  const int kb = pk.rank;  // causal: key block 0 sees every query and has the most work
+  int kb = pk.rank;  // causal: key block 0 sees every query and has the most work
+  // Block-sparse by pieces: the workgroup's item names its column and piece.
+  int piece0 = 0, slot = -1;
+  const bool by_items = SP && a.sp_items != nullptr;
+  if (by_items) {
+    const int* it4 = a.sp_items + 4 * (size_t)blockIdx.x;
+    bhk = it4[0];
+    kb = it4[1];
+    piece0 = it4[2];
+    slot = it4[3];
+  }
   const int b = bhk / a.Hkv;
   const int G = a.H / a.Hkv;
   const int g0 = share * (G / S), g1 = g0 + G / S;
@@ -186,6 +196,10 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
     n_kept = list_mask_blocks<kBwdThreads>(mcol, nb, qt_begin / 2, (qt_end + 1) / 2, blist, bwc);
     c_begin = 0;
     c_end = mask_tiles_below(blist, n_kept, qt_end);
+    if (by_items) {  // this piece: listed blocks [piece0, piece0 + kSparsePiece)
+      c_begin = min(2 * piece0, c_end);
+      c_end = min(c_end, 2 * (piece0 + kSparsePiece));
+    }
   }
   auto tile_ix = [&](int c) -> int {
     if constexpr (SP) return mask_tile(blist, c);
@@ -318,7 +332,7 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   if (blk_key0 + BK <= kv_end) it_full = a.causal ? max(qt_begin, (blk_key0 + BK - 1 + BQ - 1) / BQ) : qt_begin;
   it_full = min(it_full, qt_end);
   int c_full = it_full;  // sequence position of the first full tile
-  if constexpr (SP) c_full = mask_tiles_below(blist, n_kept, it_full);
+  if constexpr (SP) c_full = min(max(mask_tiles_below(blist, n_kept, it_full), c_begin), c_end);
   for (int g = g0; g < g1; ++g) {
     set_query_head(g);
     // Every wave is done with the previous query head's last tile before
@@ -337,7 +351,24 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   }
 
   // dK^T / dV^T accumulators: lane = key, registers = d in runs of 4.
-  if (S > 1) {
+  if (by_items && slot >= 0) {
+    // fp32 partials of this piece, rows = keys of the block
+    const size_t blk = (size_t)kMaskBlock * D;
+    float* dKp = a.dkv_part + (size_t)slot * blk + (size_t)(wave * 32 + kl) * D;
+    float* dVp = dKp + (size_t)a.sp_nslots * blk;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = dt * 32 + r4 * 8 + 4 * hh;
+        const f32x16& K4 = dk[dt];
+        const f32x16& V4 = dv[dt];
+        *(f32x4*)(dKp + d0) = f32x4{K4[4 * r4] * a.scale, K4[4 * r4 + 1] * a.scale,
+                                    K4[4 * r4 + 2] * a.scale, K4[4 * r4 + 3] * a.scale};
+        *(f32x4*)(dVp + d0) = f32x4{V4[4 * r4], V4[4 * r4 + 1], V4[4 * r4 + 2], V4[4 * r4 + 3]};
+      }
+    }
+  } else if (S > 1) {
     // fp32 partials of this share; the reduction adds the shares in order.
     if (my_key < N) {
       const size_t part = (size_t)a.B * a.Hkv * N * D;
@@ -642,6 +673,34 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* __restrict
   }
 }
 
+// dK, dV of the block-sparse columns cut into pieces: the sum of each
+// column's fp32 piece partials, in piece order, rounded once. One workgroup
+// per (column, 32 key rows); thread t covers 4 consecutive elements.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void sparse_dkv_reduce_kernel(BwdArgs a) {
+  constexpr int ROWS = 256 * 4 / D;  // key rows per workgroup (16 or 8)
+  const int col = blockIdx.x / (kMaskBlock / ROWS);
+  const int r0 = (blockIdx.x % (kMaskBlock / ROWS)) * ROWS;
+  const int* c4 = a.sp_cols + 4 * (size_t)col;
+  const int bh = c4[0], kb = c4[1], slot0 = c4[2], np = c4[3];
+  const int e = threadIdx.x * 4;               // element within ROWS x D
+  const int row = r0 + e / D, d0 = e % D;
+  const int key = kb * kMaskBlock + row;
+  if (key >= a.N) return;
+  const size_t blk = (size_t)kMaskBlock * D;
+  const float* pk = a.dkv_part + (size_t)slot0 * blk + (size_t)row * D + d0;
+  const float* pv = pk + (size_t)a.sp_nslots * blk;
+  f32x4 sk = *(const f32x4*)pk, sv = *(const f32x4*)pv;
+  for (int i = 1; i < np; ++i) {
+    const f32x4 xk = *(const f32x4*)(pk + i * blk), xv = *(const f32x4*)(pv + i * blk);
+    sk[0] += xk[0]; sk[1] += xk[1]; sk[2] += xk[2]; sk[3] += xk[3];
+    sv[0] += xv[0]; sv[1] += xv[1]; sv[2] += xv[2]; sv[3] += xv[3];
+  }
+  const size_t off = ((size_t)bh * a.N + key) * D + d0;
+  *(u32x2*)((uint16_t*)a.dk + off) = u32x2{Mfma<T>::pack(sk[0], sk[1]), Mfma<T>::pack(sk[2], sk[3])};
+  *(u32x2*)((uint16_t*)a.dv + off) = u32x2{Mfma<T>::pack(sv[0], sv[1]), Mfma<T>::pack(sv[2], sv[3])};
+}
+
 template <typename T, int D, bool SP = false>
 hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   hipError_t e = hipSuccess;
@@ -660,10 +719,15 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   }
   if (stages & (int)BwdStage::DKDV) {
     const long nkb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-    hipLaunchKernelGGL((dkdv_kernel<T, D, SP>),
-                       dim3((unsigned)((long)a.B * a.Hkv * a.gsplit * nkb)), dim3(kBwdThreads),
-                       0, st, a);
+    const long grid = (SP && a.sp_items) ? (long)a.sp_nitems : (long)a.B * a.Hkv * a.gsplit * nkb;
+    hipLaunchKernelGGL((dkdv_kernel<T, D, SP>), dim3((unsigned)grid), dim3(kBwdThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (SP && a.sp_items && a.sp_ncols > 0) {
+      hipLaunchKernelGGL((sparse_dkv_reduce_kernel<T, D>),
+                         dim3((unsigned)((long)a.sp_ncols * (kMaskBlock / (256 * 4 / D)))), dim3(256),
+                         0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (a.gsplit > 1) {
       const long long n4 = (long long)a.B * a.Hkv * a.N * D / 4;
       const long long blocks = (2 * n4 + 255) / 256 < 8192 ? (2 * n4 + 255) / 256 : 8192;

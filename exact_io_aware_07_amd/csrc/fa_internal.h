@@ -65,7 +65,20 @@ struct BwdArgs {
   // Block mask, as in FwdArgs (block-sparse instantiations only).
   const unsigned char* bmask;
   long long bm_sb, bm_sh;
+  // Block-sparse dK/dV by pieces (sp_items != nullptr): workgroup i runs
+  // item sp_items[4i .. 4i+3] = (b*H + h, key block, first listed query
+  // block, slot): the kept query blocks at list positions [first, first +
+  // kSparsePiece) of that key block's column; slot < 0 writes dK, dV, slot
+  // >= 0 writes fp32 partials [slot][kMaskBlock][d] (dK parts, then
+  // sp_nslots dV parts) to dkv_part, which the reduction adds per column
+  // (sp_cols[4c .. 4c+3] = (b*H + h, key block, first slot, pieces)).
+  const int* sp_items;
+  const int* sp_cols;
+  int sp_nitems, sp_ncols, sp_nslots;
 };
+
+// Kept query blocks per piece of a block-sparse dK/dV column.
+constexpr int kSparsePiece = 8;
 
 // Query-head split of the grouped dK/dV stage for a shape: the smallest
 // divisor of H / Hkv that gives the stage at least two workgroups per

@@ -243,6 +243,42 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o,
                   size_t workspace_bytes, void* stream, int dtype);
 
 /*
+ * Block-sparse backward with long mask columns cut into pieces. In
+ * fa_bwd_sparse one workgroup computes a key block's dK, dV over every kept
+ * query block of its mask column, so a column kept by many query blocks
+ * (a global key, the first block of a sink pattern) is one long serial job.
+ * fa_sparse_bwd_plan reads a HOST copy of the mask (same layout and
+ * strides as the device mask) and cuts every column with more than 8 kept
+ * query blocks (causal: blocks on or after the diagonal) into pieces of at
+ * most 8, longest first. fa_bwd_sparse_planned runs one workgroup per piece:
+ * pieces of a cut column write fp32 partial dK, dV to the workspace and a
+ * second launch adds them in piece order (deterministic); other columns
+ * are written as in fa_bwd_sparse, bit for bit.
+ *   fa_sparse_bwd_plan: counts in *n_items, *n_cols, *n_slots; with items
+ *   and cols NULL only the counts; else items (int32 [n_items][4]) and cols
+ *   (int32 [n_cols][4]) are filled (FA_ERR_INVALID_ARG if a capacity, in
+ *   entries of 4 ints, is too small). Host memory only, no HIP call.
+ *   fa_bwd_sparse_planned: the arguments of fa_bwd_sparse plus the plan
+ *   copied to device memory (items, cols: 4-byte aligned) and its three
+ *   counts; workspace of fa_bwd_sparse_planned_workspace_bytes(B, H, N, d,
+ *   n_slots) bytes. The plan must come from the same mask, strides, B, H,
+ *   N and causal: it is not checked on the device.
+ */
+int fa_sparse_bwd_plan(const unsigned char* host_mask, long long mask_stride_b,
+                       long long mask_stride_h, int B, int H, int N, int causal,
+                       int* items, int max_items, int* cols, int max_cols,
+                       int* n_items, int* n_cols, int* n_slots);
+size_t fa_bwd_sparse_planned_workspace_bytes(int B, int H, int N, int d, int n_slots);
+int fa_bwd_sparse_planned(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk,
+                          void* dv, int B, int H, int N, int d, float scale, int causal,
+                          const int* kv_len, const unsigned char* block_mask,
+                          long long mask_stride_b, long long mask_stride_h,
+                          const int* items, int n_items, const int* cols, int n_cols,
+                          int n_slots, void* workspace, size_t workspace_bytes,
+                          void* stream, int dtype);
+
+/*
  * FP8 forward with incoherent processing (marketmaker.cc article, section
  * "FA3：料斗力学", item 3: FP8 attention is spoiled by outliers, so the
  * vectors are rotated at random before a block-wise quantisation, which

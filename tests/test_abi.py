@@ -379,3 +379,69 @@ def test_fp8_workspace_holds_every_buffer():
     need = 2 * B * H * N * d + B * H * d * np_ + 4 * (B * H * 3 + 2 * B * H * 5 + B * H)
     got = fa.fa_fwd_fp8_workspace_bytes(B, H, N, d)
     assert need <= got <= need + 7 * 256
+
+
+def _plan_counts(mask, B, H, N, causal):
+    nb = (N + 127) // 128
+    m = mask.expand(B, H, nb, nb) if mask.dim() == 2 else mask
+    out = {}
+    for b in range(B):
+        for h in range(H):
+            for kb in range(nb):
+                lo = kb if causal else 0
+                out[(b * H + h, kb)] = int((m[b, h, lo:, kb] != 0).sum())
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sparse_plan_cuts_long_columns_into_pieces_of_eight(causal):
+    from exact_io_aware_07_amd import workloads as W
+    B, H, N = 2, 3, 128 * 40
+    mask = W.random_block_mask((B, H), N, 0.45, seed=7)
+    mask[0, 1, :, 3] = 1                      # one full column
+    mask[1, 2, :, 5] = 0                      # one empty column
+    plan = fa.fa_sparse_bwd_plan(mask, B, H, N, causal)
+    items, cols = plan["items"].tolist(), plan["cols"].tolist()
+    counts = _plan_counts(mask, B, H, N, causal)
+    seen = {}
+    for bh, kb, first, slot in items:
+        seen.setdefault((bh, kb), []).append((first, slot))
+    assert set(seen) == set(counts)           # every key block of every head, once or in pieces
+    col_of = {(c[0], c[1]): c for c in cols}
+    sizes = []
+    for key, n in counts.items():
+        got = sorted(seen[key])
+        if n <= 8:
+            assert got == [(0, -1)] and key not in col_of
+            sizes.append(n)
+            continue
+        pieces = -(-n // 8)
+        bh, kb, slot0, np_ = col_of[key]
+        assert np_ == pieces and got == [(8 * i, slot0 + i) for i in range(pieces)]
+        sizes += [min(8, n - 8 * i) for i in range(pieces)]
+    assert plan["n_slots"] == sum(c[3] for c in cols)
+    assert sorted(c[2] for c in cols) == [sum(x[3] for x in cols if x[2] < c[2]) for c in sorted(cols, key=lambda c: c[2])]
+    # longest pieces first
+    size_of = lambda it: min(8, counts[(it[0], it[1])] - it[2]) if counts[(it[0], it[1])] > 8 else counts[(it[0], it[1])]
+    order = [size_of(it) for it in items]
+    assert order == sorted(order, reverse=True) and sorted(order) == sorted(sizes)
+
+
+def test_sparse_plan_validation_and_counts_only():
+    L = fa.lib()
+    n = [ctypes.c_int(0) for _ in range(3)]
+    r = lambda *a: L.fa_sparse_bwd_plan(*a, *(ctypes.byref(x) for x in n))
+    assert r(None, 0, 0, 1, 1, 300, 0, None, 0, None, 0) == fa.FA_ERR_INVALID_ARG     # mask missing
+    m = (ctypes.c_ubyte * 9)(*([1] * 9))
+    assert r(m, 0, 0, 1, 1, 300, 2, None, 0, None, 0) == fa.FA_ERR_INVALID_ARG        # causal 2
+    assert r(m, -1, 0, 1, 1, 300, 0, None, 0, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert r(m, 0, 0, 1, 1, 300, 0, None, 0, None, 0) == fa.FA_OK
+    assert [x.value for x in n] == [3, 0, 0]
+    items = (ctypes.c_int * 8)()
+    cols = (ctypes.c_int * 4)()
+    assert r(m, 0, 0, 1, 1, 300, 0, items, 2, cols, 1) == fa.FA_ERR_INVALID_ARG       # 3 items, room for 2
+    assert fa.fa_bwd_sparse_planned_workspace_bytes(1, 2, 300, 64, 3) == 2 * 300 * 4 + 2 * 3 * 128 * 64 * 4 + 256 - (2 * 300 * 4) % 256
+    assert L.fa_bwd_sparse_planned(*([A] * 9), 1, 2, 300, 64, 0.125, 0, None, A, 0, 0, A, 2, A, 0, 0,
+                                   A, 1 << 20, None, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG  # 2 items < 3 key blocks
+    assert L.fa_bwd_sparse_planned(*([A] * 9), 1, 2, 300, 64, 0.125, 0, None, A, 0, 0, A, 6, A, 1, 0,
+                                   A, 1 << 20, None, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG  # cols without slots

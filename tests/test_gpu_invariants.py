@@ -87,3 +87,45 @@ def test_no_score_matrix_is_allocated(wname):
     assert free0 - free1 < forbidden // 64, (free0 - free1, forbidden)
     # the caller-owned workspace is O(N): one fp32 per row
     assert ws.numel() == w.B * w.H * w.N * 4 < forbidden
+
+
+def test_every_other_entry_point_allocates_nothing():
+    """The key-split, grouped-query, block-sparse and FP8 paths, each given
+    its workspace: no torch allocation during the calls and no change in the
+    device's free memory (the library never allocates)."""
+    from exact_io_aware_07_amd import (fa_bwd_gqa, fa_bwd_gqa_workspace_bytes, fa_bwd_sparse,
+                                       fa_bwd_workspace_bytes, fa_fwd_fp8_incoherent,
+                                       fa_fwd_fp8_workspace_bytes, fa_fwd_gqa, fa_fwd_sparse,
+                                       fa_fwd_split, fa_fwd_split_workspace_bytes)
+    B, H, Hkv, N, d = 2, 8, 2, 2048, 128
+    say("memory of the split, GQA, sparse and FP8 paths")
+    inp = W.random_case(B, H, N, d, "bf16", seed=30, backward=True)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    kg, vg = k[:, :Hkv].contiguous(), v[:, :Hkv].contiguous()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dkg, dvg = torch.empty_like(kg), torch.empty_like(vg)
+    mask = W.random_block_mask((), N, 0.5, seed=31).cuda()
+    signs = W.random_signs(d, seed=32).cuda()
+    ws_bytes = max(fa_fwd_split_workspace_bytes(B, H, N, d, 4), fa_bwd_gqa_workspace_bytes(B, H, Hkv, N, d),
+                   fa_bwd_workspace_bytes(B, H, N, d), fa_fwd_fp8_workspace_bytes(B, H, N, d))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def calls():
+        fa_fwd_split(q, k, v, o, lse, 0.1, True, None, 4, ws)
+        fa_fwd_gqa(q, kg, vg, o, lse, 0.1, True)
+        fa_bwd_gqa(q, kg, vg, o, do, lse, dq, dkg, dvg, 0.1, True, None, ws)
+        fa_fwd_sparse(q, k, v, o, lse, mask, 0.1, False)
+        fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, mask, 0.1, False, None, ws)
+        fa_fwd_fp8_incoherent(q, k, v, signs, o, lse, 0.1, False, None, ws)
+
+    calls()  # code objects load
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    free0 = _free_bytes()
+    calls()
+    free1 = _free_bytes()
+    assert torch.cuda.max_memory_allocated() == before
+    # a score matrix of one call would take B*H*N^2*2 bytes (134 MB here)
+    assert free0 - free1 < B * H * N * N * 2 // 64, (free0, free1)

@@ -163,3 +163,69 @@ def test_measurement_shape_sampled_against_oracle():
         e = rel_fro(np64(got), ref)
         print(f"full size {name} rel-fro {e:.2e}", flush=True)
         assert e <= GRAD_REL_FRO, (name, e)
+
+
+def planned(inp, mask, scale, causal):
+    """fa_fwd_sparse, then the backward by the host plan of the mask."""
+    from exact_io_aware_07_amd import fa_bwd_sparse_planned, fa_sparse_bwd_plan
+    q, k, v, do, kv = (dev(inp[n]) for n in ("q", "k", "v", "do", "kv_len"))
+    B, H, N, d = q.shape
+    plan = fa_sparse_bwd_plan(mask.contiguous(), B, H, N, causal)
+    m = mask.contiguous().cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    fa_fwd_sparse(q, k, v, o, lse, m, scale, causal, kv)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    fa_bwd_sparse_planned(q, k, v, o, do, lse, *grads, m, plan, scale, causal, kv)
+    torch.cuda.synchronize()
+    return o, lse, grads, plan
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_planned_backward_without_long_columns_is_the_same_bits(causal):
+    B, H, N, d = 2, 2, 1000, 64       # 8 blocks: no column holds more than 8
+    say(f"sparse planned, no cut column, causal={causal}")
+    inp = W.random_case(B, H, N, d, "bf16", seed=40, causal=causal, backward=True)
+    mask = W.random_block_mask((B, H), N, 0.7, seed=41)
+    _, _, g1, plan = planned(inp, mask, d ** -0.5, causal)
+    assert plan["n_slots"] == 0
+    _, _, g2 = run(inp, mask, d ** -0.5, causal)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_planned_backward_with_long_columns_matches_oracle(d, causal):
+    B, H, N = 1, 2, 2100                 # 17 blocks
+    say(f"sparse planned, cut columns d={d} causal={causal}")
+    inp = W.random_case(B, H, N, d, "bf16", seed=42 + d, causal=causal, backward=True, kv_len=[1900])
+    mask = W.random_block_mask((B, H), N, 0.6, seed=43)
+    mask[0, 0, :, 0] = 1
+    mask[0, 1, :, 2] = 1
+    o, lse, grads, plan = planned(inp, mask, d ** -0.5, causal)
+    assert plan["n_slots"] > 0
+    ref = attn_bwd64_sparse(inp["q"], inp["k"], inp["v"], inp["do"], d ** -0.5, causal, [1900], mask.numpy())
+    check_grads(grads, ref, f"planned d={d}")
+    _, _, g2 = run(inp, mask, d ** -0.5, causal)
+    for a, b in zip(grads, g2):  # same gradients, other summation order where cut
+        assert rel_fro(np64(a), np64(b)) < 5e-3
+
+
+def test_planned_backward_measurement_shape_sampled_against_oracle():
+    w = W.SPARSE
+    say(f"sparse planned full size {w.name}")
+    inp = W.make_inputs(w, seed=0)
+    mask = W.block_mask(w)
+    _, _, grads, plan = planned(inp, mask, w.scale, w.causal)
+    assert plan["n_slots"] == w.H * 16      # the first key block, kept by all 128 query blocks
+    rows = [0, 1, 127, 128, 129, 5000, 8191, 8192, 16000, w.N - 1]
+    h = 11
+    sq, sk, sv = attn_bwd64_sparse_sampled(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.causal,
+                                           None, mask.numpy(), [(0, h)], rows, rows)
+    dq, dk, dv = grads
+    for name, got, ref in (("dq", dq[0, h, rows], sq[0]), ("dk", dk[0, h, rows], sk[0]),
+                           ("dv", dv[0, h, rows], sv[0])):
+        e = rel_fro(np64(got), ref)
+        print(f"planned full size {name} rel-fro {e:.2e}", flush=True)
+        assert e <= GRAD_REL_FRO, (name, e)
