@@ -191,9 +191,14 @@ def attn_bwd64_sampled(q, k, v, dout, scale: float, causal: bool = False, kv_len
     all_rows = np.arange(N)
     for t, (b, h) in enumerate(pairs):
         lim = int(lens[b])
-        lse = np.empty(N)
-        dsum = np.empty(N)
-        for c0 in range(0, N, row_chunk):
+        lse = np.full(N, -np.inf)
+        dsum = np.zeros(N)
+        # D_i of every row is needed only for dK / dV (columns); dQ rows
+        # need their own D_i, which their own P rows give. Under the causal
+        # mask a row before the first requested key sees none of them
+        # (P = 0 there), so the pass starts at that key.
+        row0 = int(kr.min()) if (causal and len(kr)) else 0
+        for c0 in range(row0, N if len(kr) else row0, row_chunk):
             rr = all_rows[c0:c0 + row_chunk]
             _, l_c, p_c = _rows_forward(q[b, h, rr], k[b, h], v[b, h], rr, scale, causal, lim)
             dp_c = dout[b, h, rr] @ v[b, h].T
@@ -202,10 +207,11 @@ def attn_bwd64_sampled(q, k, v, dout, scale: float, causal: bool = False, kv_len
         if len(qr):
             _, _, p_r = _rows_forward(q[b, h, qr], k[b, h], v[b, h], qr, scale, causal, lim)
             dp_r = dout[b, h, qr] @ v[b, h].T
-            dq[t] = scale * ((p_r * (dp_r - dsum[qr, None])) @ k[b, h])
+            d_r = (p_r * dp_r).sum(axis=1)
+            dq[t] = scale * ((p_r * (dp_r - d_r[:, None])) @ k[b, h])
         if len(kr):
             s_c = scale * (q[b, h] @ k[b, h, kr].T)                  # [N, C] columns of S
-            vis = visible_mask(all_rows, N, causal, lim)[:, kr]
+            vis = (kr[None, :] < lim) & ((kr[None, :] <= all_rows[:, None]) if causal else True)
             has_key = np.isfinite(lse)
             lse_safe = np.where(has_key, lse, 0.0)
             p_c = np.where(vis & has_key[:, None], np.exp(s_c - lse_safe[:, None]), 0.0)

@@ -1,0 +1,57 @@
+"""The longest sequences: sizes where every 32-bit byte offset inside a head
+is large and the grid is long, checked where the fp64 oracle can follow.
+
+  * forward at 1,048,576 tokens (causal, one head): O and LSE of sampled
+    rows against the oracle, each row against all its keys;
+  * backward at 262,144 tokens (causal, one head): dQ of sampled rows and
+    dK, dV of the last keys (which only the last rows see) against the
+    oracle, and for all of dV the identity that holds at any size:
+    sum_j dV_j = sum_i dO_i (each row's probabilities sum to one).
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_07_amd import workloads as W
+from helpers import FWD_MAX_ABS, GRAD_REL_FRO, LSE_MAX_ABS, fwd_stats, np64, rel_fro, run_bwd, run_fwd, say
+from oracle import attn_bwd64_sampled, attn_fwd64
+
+pytestmark = pytest.mark.gpu
+
+
+def test_forward_at_a_million_tokens():
+    N, d = 1 << 20, 64
+    say(f"long forward N={N}")
+    inp = W.random_case(1, 1, N, d, "bf16", seed=50, causal=True)
+    o, lse = run_fwd(inp, d ** -0.5, True, out_dtype=torch.float32)
+    rows = [0, 1, 127, 128, 65535, 65536, 500000, N // 2, N - 129, N - 128, N - 2, N - 1]
+    o_ref, lse_ref = attn_fwd64(inp["q"], inp["k"], inp["v"], d ** -0.5, True, rows=rows, row_chunk=4)
+    st = fwd_stats(np64(o[:, :, rows]), np64(lse[:, :, rows]), o_ref, lse_ref)
+    print(f"N={N} {st}", flush=True)
+    assert st["max_abs"] <= FWD_MAX_ABS and st["lse_max_abs"] <= LSE_MAX_ABS, st
+
+
+def test_backward_at_262144_tokens():
+    N, d = 1 << 18, 64
+    say(f"long backward N={N}")
+    inp = W.random_case(1, 1, N, d, "bf16", seed=51, causal=True, backward=True)
+    o, lse = run_fwd(inp, d ** -0.5, True)
+    dq, dk, dv = run_bwd(inp, o, lse, d ** -0.5, True)
+    rows = [0, 1, 127, 128, 100000, N // 2, N - 1]
+    keys = [N - 1, N - 2, N - 64, N - 65, N - 128, N - 129, N - 200]
+    sq, _, _ = attn_bwd64_sampled(inp["q"], inp["k"], inp["v"], inp["do"], d ** -0.5, True,
+                                  heads=[(0, 0)], q_rows=rows, k_rows=[], row_chunk=4)
+    _, sk, sv = attn_bwd64_sampled(inp["q"], inp["k"], inp["v"], inp["do"], d ** -0.5, True,
+                                   heads=[(0, 0)], q_rows=[], k_rows=keys, row_chunk=64)
+    errs = {"dq": rel_fro(np64(dq[0, 0, rows]), sq[0]), "dk": rel_fro(np64(dk[0, 0, keys]), sk[0]),
+            "dv": rel_fro(np64(dv[0, 0, keys]), sv[0])}
+    print(f"N={N} rel-fro {errs}", flush=True)
+    for n, e in errs.items():
+        assert e <= GRAD_REL_FRO, (n, e)
+    # each row's probabilities sum to one: sum_j dV_j = sum_i dO_i, up to the
+    # bf16 rounding of P (2^-9 of each row's sum) and of each dV row
+    dv_sum = np64(dv[0, 0]).sum(axis=0)
+    do_abs = np.abs(np64(inp["do"][0, 0])).sum(axis=0)
+    dv_abs = np.abs(np64(dv[0, 0])).sum(axis=0)
+    gap = np.abs(dv_sum - np64(inp["do"][0, 0]).sum(axis=0))
+    assert np.all(gap <= 2 ** -8 * (do_abs + dv_abs)), gap.max()

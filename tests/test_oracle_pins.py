@@ -287,3 +287,23 @@ def test_sampled_backward_matches_finite_differences_and_full(causal):
         np.testing.assert_allclose(sq[t], dq[b, h, rows], rtol=0, atol=1e-12)
         np.testing.assert_allclose(sk[t], dk[b, h, keys], rtol=0, atol=1e-12)
         np.testing.assert_allclose(sv[t], dv[b, h, keys], rtol=0, atol=1e-12)
+    # dQ rows alone (no keys asked for): the same numbers without the pass over every row
+    sq2, sk2, _ = attn_bwd64_sampled(q, k, v, do, 0.3, causal, kv, heads=[(1, 1), (0, 1)],
+                                     q_rows=rows, k_rows=[], row_chunk=32)
+    assert sk2.shape == (2, 0, d)
+    for t, (b, h) in enumerate([(1, 1), (0, 1)]):
+        np.testing.assert_allclose(sq2[t], dq[b, h, rows], rtol=0, atol=1e-12)
+
+
+def test_sampled_backward_of_late_keys_under_the_causal_mask():
+    """Keys near the end (causal): only the rows from the first such key on
+    are passed over; the result is the whole backward's."""
+    from oracle import attn_bwd64_sampled
+    B, H, N, d = 1, 1, 70, 4
+    q, k, v, do = (_rand((B, H, N, d), 120 + s) for s in range(4))
+    dq, dk, dv = attn_bwd64(q, k, v, do, 0.5, True)
+    keys = [69, 60, 55]
+    _, sk, sv = attn_bwd64_sampled(q, k, v, do, 0.5, True, heads=[(0, 0)], q_rows=[], k_rows=keys,
+                                   row_chunk=8)
+    np.testing.assert_allclose(sk[0], dk[0, 0, keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sv[0], dv[0, 0, keys], rtol=0, atol=1e-12)
