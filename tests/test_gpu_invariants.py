@@ -129,3 +129,25 @@ def test_every_other_entry_point_allocates_nothing():
     assert torch.cuda.max_memory_allocated() == before
     # a score matrix of one call would take B*H*N^2*2 bytes (134 MB here)
     assert free0 - free1 < B * H * N * N * 2 // 64, (free0, free1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_leaves_o_and_shifts_lse(causal):
+    """Adding u to every key row adds scale * q_i . u to every score of row i:
+    O is unchanged and LSE_i moves by that amount. fp16 keys on a 1/16 grid
+    in [-4, 4] and u = 64 keep K + u exact in fp16; the scores become large,
+    which drives the running maximum."""
+    B, H, N, d = 2, 2, 300, 64
+    say(f"key shift causal={causal}")
+    g = torch.Generator().manual_seed(60)
+    inp = W.random_case(B, H, N, d, "fp16", seed=61)
+    inp["k"] = (torch.randint(-64, 65, (B, H, N, d), generator=g).float() / 16).to(torch.float16)
+    u = 64.0
+    shifted = dict(inp, k=(inp["k"].float() + u).to(torch.float16))
+    assert torch.equal(shifted["k"].float(), inp["k"].float() + u)
+    scale = d ** -0.5
+    o1, l1 = run_fwd(inp, scale, causal, out_dtype=torch.float32)
+    o2, l2 = run_fwd(shifted, scale, causal, out_dtype=torch.float32)
+    shift = scale * u * inp["q"].double().sum(dim=-1).numpy()
+    assert np.abs(np64(o2) - np64(o1)).max() <= 1e-2
+    assert np.abs(np64(l2) - np64(l1) - shift).max() <= 1e-3 * max(1.0, np.abs(shift).max() / 64)
