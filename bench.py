@@ -237,7 +237,8 @@ def run_gpu(args):
         out["extra"] = extra_configs(torch, W)
         out["extra"][W.FEW_HEADS.name] = split_config(torch, W)
         out["extra"][W.GQA.name] = gqa_config(torch, W)
-        out["extra"][W.SPARSE.name] = sparse_config(torch, W)
+        for sw in (W.SPARSE, W.SPARSE_GLOBAL):
+            out["extra"][sw.name] = sparse_config(torch, W, sw)
         out["extra"][W.FP8.name] = fp8_config(torch, W)
     return out
 
@@ -300,15 +301,16 @@ def median_ms(torch, fn, iters: int = 10) -> float:
     return statistics.median(batches)
 
 
-def sparse_config(torch, W):
-    """Block-sparse attention on its band-and-first-block mask: forward and
-    backward through fa_fwd_sparse / fa_bwd_sparse, TFLOP/s counted on the
-    kept (query, key) pairs only, and the dense entry points on the same
-    inputs for the speed-up (ideal: 1 / kept fraction)."""
+def sparse_config(torch, W, w):
+    """Block-sparse attention on one of its masks: forward and backward
+    through fa_fwd_sparse / fa_bwd_sparse and through the planned entry
+    points (long mask lines cut into pieces), TFLOP/s counted on the kept
+    (query, key) pairs only, and the dense entry points on the same inputs
+    for the speed-up (ideal: 1 / kept fraction)."""
     from exact_io_aware_07_amd import (fa_bwd, fa_bwd_sparse, fa_bwd_sparse_planned,
                                        fa_bwd_sparse_planned_workspace_bytes, fa_fwd, fa_fwd_sparse,
-                                       fa_sparse_bwd_plan)
-    w = W.SPARSE
+                                       fa_fwd_sparse_planned, fa_fwd_sparse_planned_workspace_bytes,
+                                       fa_sparse_plan)
     inp = W.make_inputs(w)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
     mask = W.block_mask(w).cuda()
@@ -320,18 +322,25 @@ def sparse_config(torch, W):
     kept = float(mask.sum().item()) * W.MASK_BLOCK * W.MASK_BLOCK * w.B * w.H
     fwd_kept = 4.0 * w.d * kept
     fa_fwd_sparse(q, k, v, o, lse, mask, w.scale, w.causal)
-    plan = fa_sparse_bwd_plan(W.block_mask(w), w.B, w.H, w.N, w.causal)
-    plan = {"items": plan["items"].cuda(), "cols": plan["cols"].cuda(), "n_slots": plan["n_slots"]}
-    ws_p = torch.empty(fa_bwd_sparse_planned_workspace_bytes(w.B, w.H, w.N, w.d, plan["n_slots"]),
+    plan = fa_sparse_plan(W.block_mask(w), w.B, w.H, w.N, w.causal)
+    plan = {"plan": plan["plan"].cuda(), "counts": plan["counts"]}
+    ws_f = torch.empty(max(fa_fwd_sparse_planned_workspace_bytes(w.B, w.H, w.N, w.d, plan["counts"]), 16),
                        dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(fa_bwd_sparse_planned_workspace_bytes(w.B, w.H, w.N, w.d, plan["counts"]),
+                       dtype=torch.uint8, device="cuda")
+    o_p, lse_p = torch.empty_like(o), torch.empty_like(lse)
     runs = {
         "fwd_sparse": (lambda: fa_fwd_sparse(q, k, v, o, lse, mask, w.scale, w.causal), 1.0),
+        "fwd_sparse_planned": (lambda: fa_fwd_sparse_planned(q, k, v, o_p, lse_p, mask, plan, w.scale,
+                                                             w.causal, None, ws_f), 1.0),
         "bwd_sparse": (lambda: fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, mask, w.scale,
                                              w.causal, None, ws), 2.5),
         "bwd_sparse_planned": (lambda: fa_bwd_sparse_planned(q, k, v, o, do, lse, dq, dk, dv, mask, plan,
-                                                             w.scale, w.causal, None, ws_p), 2.5),
+                                                             w.scale, w.causal, None, ws_b), 2.5),
     }
-    entry = {"kept_fraction": kept / (w.B * w.H * w.N * w.N), "mask": w.block_pattern}
+    c = plan["counts"].tolist()
+    entry = {"kept_fraction": kept / (w.B * w.H * w.N * w.N), "mask": w.block_pattern,
+             "plan_pieces": {"col_slots": c[2], "row_slots": c[5]}}
     for name, (fn, mult) in runs.items():
         ms = median_ms(torch, fn)
         rate = mult * fwd_kept / (ms * 1e-3)
@@ -345,9 +354,9 @@ def sparse_config(torch, W):
                                             None, ws)}
     for name, fn in dense.items():
         entry[name] = median_ms(torch, fn)
-    entry["fwd_speedup_vs_dense"] = entry["fwd_dense_ms"] / entry["fwd_sparse_ms"]
-    entry["bwd_speedup_vs_dense"] = entry["bwd_dense_ms"] / entry["bwd_sparse_ms"]
-    entry["bwd_planned_speedup_vs_dense"] = entry["bwd_dense_ms"] / entry["bwd_sparse_planned_ms"]
+    for p in ("fwd", "bwd"):
+        for v_ in ("sparse", "sparse_planned"):
+            entry[f"{p}_{v_}_speedup_vs_dense"] = entry[f"{p}_dense_ms"] / entry[f"{p}_{v_}_ms"]
     log(f"[bench] extra {w.name}: {entry}")
     return entry
 
@@ -542,20 +551,23 @@ def profile_workload(name: str, iters: int) -> None:
     from exact_io_aware_07_amd import attention_backward, attention_forward, lib
     from exact_io_aware_07_amd import workloads as W
     lib()
-    from exact_io_aware_07_amd import fa_bwd_sparse, fa_fwd_fp8_incoherent, fa_fwd_sparse
+    from exact_io_aware_07_amd import (fa_bwd_sparse_planned, fa_fwd_fp8_incoherent,
+                                       fa_fwd_sparse_planned, fa_sparse_plan)
     w = W.ALL[name]
     inp = {n: (t.cuda() if t is not None else None) for n, t in W.make_inputs(w).items()}
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     fwd_ms, bwd_ms = [], []
     mask = W.block_mask(w)
-    mask = None if mask is None else mask.cuda()
+    if mask is not None:          # block-sparse: the planned entry points
+        plan = fa_sparse_plan(mask, w.B, w.H, w.N, w.causal)
+        mask = mask.cuda()
     signs = W.random_signs(w.d, seed=0).cuda() if w.ch_outliers else None
     for _ in range(iters):
         ev[0].record()
         if mask is not None:      # block-sparse
             o = torch.empty_like(inp["q"])
             lse = torch.empty(inp["q"].shape[:3], dtype=torch.float32, device="cuda")
-            fa_fwd_sparse(inp["q"], inp["k"], inp["v"], o, lse, mask, w.scale, w.causal)
+            fa_fwd_sparse_planned(inp["q"], inp["k"], inp["v"], o, lse, mask, plan, w.scale, w.causal)
         elif signs is not None:   # FP8 with the rotation
             o = torch.empty_like(inp["q"])
             lse = torch.empty(inp["q"].shape[:3], dtype=torch.float32, device="cuda")
@@ -565,7 +577,8 @@ def profile_workload(name: str, iters: int) -> None:
         ev[1].record()
         if w.backward and mask is not None:
             g = [torch.empty_like(inp["q"]) for _ in range(3)]
-            fa_bwd_sparse(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, *g, mask, w.scale, w.causal)
+            fa_bwd_sparse_planned(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, *g, mask, plan, w.scale,
+                                  w.causal)
         elif w.backward:
             attention_backward(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, w.causal,
                                inp["kv_len"], w.scale)

@@ -396,95 +396,162 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
                     mask_stride_b, mask_stride_h);
 }
 
-int fa_sparse_bwd_plan(const unsigned char* host_mask, long long mask_stride_b,
-                       long long mask_stride_h, int B, int H, int N, int causal, int* items,
-                       int max_items, int* cols, int max_cols, int* n_items, int* n_cols,
-                       int* n_slots) {
-  if (B < 0 || H < 0 || N < 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
-  if (mask_stride_b < 0 || mask_stride_h < 0 || !n_items || !n_cols || !n_slots)
-    return FA_ERR_INVALID_ARG;
-  const int nb = (N + fa::kMaskBlock - 1) / fa::kMaskBlock;
-  if (nb > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
-  if ((long long)B * H * N > 0 && !host_mask) return FA_ERR_INVALID_ARG;
-  struct Item { int bh, kb, first, slot, size; };
-  std::vector<Item> its;
-  std::vector<int> cs;
-  int slots = 0;
+// Plan of the block-sparse entry points by pieces: counts[8] = {column
+// items, cut columns, column slots, row items, cut rows, row slots, 0, 0};
+// plan = column items, cut columns, row items, cut rows, 4 ints each.
+namespace {
+struct SparseItem { int bh, blk, first, slot, size; };
+
+// Items of one kind (columns: the query blocks of key block j; rows: the
+// key blocks of query block i) and the cut lines, longest pieces first.
+void sparse_pieces(const unsigned char* host_mask, long long sb, long long sh, int B, int H, int nb,
+                   int causal, bool columns, std::vector<SparseItem>& its, std::vector<int>& cut,
+                   int* slots) {
   const int C = fa::kSparsePiece;
-  for (int b = 0; b < B && N > 0; ++b) {
+  *slots = 0;
+  for (int b = 0; b < B; ++b) {
     for (int h = 0; h < H; ++h) {
-      const unsigned char* m = host_mask + b * mask_stride_b + h * mask_stride_h;
-      for (int kb = 0; kb < nb; ++kb) {
+      const unsigned char* m = host_mask + b * sb + h * sh;
+      for (int x = 0; x < nb; ++x) {
         int n = 0;
-        for (int qb = causal ? kb : 0; qb < nb; ++qb) n += m[(long long)qb * nb + kb] != 0;
+        if (columns) {  // key block x: query blocks from the diagonal on when causal
+          for (int qb = causal ? x : 0; qb < nb; ++qb) n += m[(long long)qb * nb + x] != 0;
+        } else {        // query block x: key blocks up to the diagonal when causal
+          for (int kb = 0; kb <= (causal ? x : nb - 1); ++kb) n += m[(long long)x * nb + kb] != 0;
+        }
         const int bh = b * H + h;
         if (n <= C) {
-          its.push_back({bh, kb, 0, -1, n});
+          its.push_back({bh, x, 0, -1, n});
           continue;
         }
         const int pieces = (n + C - 1) / C;
-        for (int i = 0; i < pieces; ++i) its.push_back({bh, kb, i * C, slots + i, std::min(C, n - i * C)});
-        cs.insert(cs.end(), {bh, kb, slots, pieces});
-        slots += pieces;
+        for (int i = 0; i < pieces; ++i)
+          its.push_back({bh, x, i * C, *slots + i, std::min(C, n - i * C)});
+        cut.insert(cut.end(), {bh, x, *slots, pieces});
+        *slots += pieces;
       }
     }
   }
-  // longest pieces first, so that they do not start last
-  std::stable_sort(its.begin(), its.end(), [](const Item& x, const Item& y) { return x.size > y.size; });
-  *n_items = (int)its.size();
-  *n_cols = (int)cs.size() / 4;
-  *n_slots = slots;
-  if (!items && !cols) return FA_OK;  // counts only
-  if (!items || !cols || max_items < *n_items || max_cols < *n_cols) return FA_ERR_INVALID_ARG;
-  for (size_t i = 0; i < its.size(); ++i) {
-    items[4 * i] = its[i].bh;
-    items[4 * i + 1] = its[i].kb;
-    items[4 * i + 2] = its[i].first;
-    items[4 * i + 3] = its[i].slot;
+  std::stable_sort(its.begin(), its.end(),
+                   [](const SparseItem& p, const SparseItem& q) { return p.size > q.size; });
+}
+
+// Host checks shared by the planned entry points; plan offsets in ints.
+int check_plan(int B, int H, int N, const int* plan, const int* counts) {
+  if (!counts) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < 6; ++i)
+    if (counts[i] < 0) return FA_ERR_INVALID_ARG;
+  if ((counts[1] > 0) != (counts[2] > 0) || (counts[4] > 0) != (counts[5] > 0))
+    return FA_ERR_INVALID_ARG;
+  const long long lines = (long long)B * H * ((N + fa::kMaskBlock - 1) / fa::kMaskBlock);
+  if ((long long)B * H * N > 0 && (counts[0] < lines || counts[3] < lines || !plan || !aligned4(plan)))
+    return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+}  // namespace
+
+int fa_sparse_plan(const unsigned char* host_mask, long long mask_stride_b, long long mask_stride_h,
+                   int B, int H, int N, int causal, int* plan, long long plan_ints, int* counts) {
+  if (B < 0 || H < 0 || N < 0 || (causal != 0 && causal != 1) || !counts) return FA_ERR_INVALID_ARG;
+  if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
+  const int nb = (N + fa::kMaskBlock - 1) / fa::kMaskBlock;
+  if (nb > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N > 0 && !host_mask) return FA_ERR_INVALID_ARG;
+  std::vector<SparseItem> ci, ri;
+  std::vector<int> cc, rc;
+  int cs = 0, rs = 0;
+  if (N > 0) {
+    sparse_pieces(host_mask, mask_stride_b, mask_stride_h, B, H, nb, causal, true, ci, cc, &cs);
+    sparse_pieces(host_mask, mask_stride_b, mask_stride_h, B, H, nb, causal, false, ri, rc, &rs);
   }
-  std::copy(cs.begin(), cs.end(), cols);
+  const int c[8] = {(int)ci.size(), (int)cc.size() / 4, cs, (int)ri.size(), (int)rc.size() / 4, rs, 0, 0};
+  std::copy(c, c + 8, counts);
+  if (!plan) return FA_OK;  // counts only
+  const long long need = 4LL * (c[0] + c[1] + c[3] + c[4]);
+  if (plan_ints < need) return FA_ERR_INVALID_ARG;
+  int* w = plan;
+  for (const auto& it : ci) { *w++ = it.bh; *w++ = it.blk; *w++ = it.first; *w++ = it.slot; }
+  w = std::copy(cc.begin(), cc.end(), w);
+  for (const auto& it : ri) { *w++ = it.bh; *w++ = it.blk; *w++ = it.first; *w++ = it.slot; }
+  std::copy(rc.begin(), rc.end(), w);
   return FA_OK;
 }
 
-size_t fa_bwd_sparse_planned_workspace_bytes(int B, int H, int N, int d, int n_slots) {
-  if (B < 0 || H < 0 || N < 0 || n_slots < 0 || (d != 64 && d != 128)) return 0;
+size_t fa_fwd_sparse_planned_workspace_bytes(int B, int H, int N, int d, const int* counts) {
+  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128) || !counts || counts[5] < 0) return 0;
+  return (size_t)counts[5] * fa::kMaskBlock * (size_t)(d + 1) * sizeof(float);
+}
+
+int fa_fwd_sparse_planned(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                          int H, int N, int d, float scale, int causal, const int* kv_len,
+                          const unsigned char* block_mask, long long mask_stride_b,
+                          long long mask_stride_h, const int* plan, const int* counts,
+                          void* workspace, size_t workspace_bytes, void* stream, int in_dtype,
+                          int o_dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (in_dtype != FA_F16 && in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((N + fa::kMaskBlock - 1) / fa::kMaskBlock > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
+  if ((st = check_plan(B, H, N, plan, counts)) != FA_OK) return st;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !block_mask) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  if (counts[5] > 0 && (!workspace || !aligned16(workspace) ||
+                        workspace_bytes < fa_fwd_sparse_planned_workspace_bytes(B, H, N, d, counts)))
+    return FA_ERR_WORKSPACE;
+  const int* row_items = plan + 4LL * (counts[0] + counts[1]);
+  fa::FwdArgs a{q, k, v, o, lse, kv_len, B, H, N, d, scale, causal, N, 0, 0, 1, N, 0, 0, H,
+                block_mask, mask_stride_b, mask_stride_h, row_items, row_items + 4LL * counts[3],
+                counts[3], counts[4], counts[5], (float*)workspace};
+  hipError_t e = fa::launch_fwd_mfma_sparse(a, elem(in_dtype), elem(o_dtype), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_sparse_planned_workspace_bytes(int B, int H, int N, int d, const int* counts) {
+  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128) || !counts || counts[2] < 0 || counts[5] < 0)
+    return 0;
   return dsum_bytes_aligned(B, H, N) +
-         2 * (size_t)n_slots * fa::kMaskBlock * (size_t)d * sizeof(float);
+         up256(2 * (size_t)counts[2] * fa::kMaskBlock * (size_t)d * sizeof(float)) +
+         (size_t)counts[5] * fa::kMaskBlock * (size_t)d * sizeof(float);
 }
 
 int fa_bwd_sparse_planned(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                           int H, int N, int d, float scale, int causal, const int* kv_len,
                           const unsigned char* block_mask, long long mask_stride_b,
-                          long long mask_stride_h, const int* items, int n_items,
-                          const int* cols, int n_cols, int n_slots, void* workspace,
-                          size_t workspace_bytes, void* stream, int dtype) {
+                          long long mask_stride_h, const int* plan, const int* counts,
+                          void* workspace, size_t workspace_bytes, void* stream, int dtype) {
   int st = check_scalars(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if ((N + fa::kMaskBlock - 1) / fa::kMaskBlock > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
   if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
-  if (n_items < 0 || n_cols < 0 || n_slots < 0 || (n_cols > 0) != (n_slots > 0))
-    return FA_ERR_INVALID_ARG;
+  if ((st = check_plan(B, H, N, plan, counts)) != FA_OK) return st;
   if ((long long)B * H * N == 0) return FA_OK;
-  // every key block of every head has at least one item
-  if ((long long)n_items < (long long)B * H * ((N + fa::kMaskBlock - 1) / fa::kMaskBlock))
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !block_mask)
     return FA_ERR_INVALID_ARG;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !block_mask || !items)
-    return FA_ERR_INVALID_ARG;
-  if (n_cols > 0 && !cols) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse) || !aligned4(items) ||
-      (cols && !aligned4(cols)))
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
     return FA_ERR_INVALID_ARG;
   if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace) ||
-      workspace_bytes < fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, n_slots))
+      workspace_bytes < fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, counts))
     return FA_ERR_WORKSPACE;
-  float* part = (float*)((char*)workspace + dsum_bytes_aligned(B, H, N));
+  char* w = (char*)workspace;
+  float* kv_part = (float*)(w + dsum_bytes_aligned(B, H, N));
+  float* q_part = (float*)((char*)kv_part + up256(2 * (size_t)counts[2] * fa::kMaskBlock * d * 4));
+  const int* col_items = plan;
+  const int* cols = plan + 4LL * counts[0];
+  const int* row_items = cols + 4LL * counts[1];
+  const int* rows = row_items + 4LL * counts[3];
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d, scale,
-                causal, H, 1, part, block_mask, mask_stride_b, mask_stride_h, items, cols,
-                n_items, n_cols, n_slots};
+                causal, H, 1, kv_part, block_mask, mask_stride_b, mask_stride_h, col_items, cols,
+                counts[0], counts[1], counts[2], row_items, rows, counts[3], counts[4], counts[5],
+                q_part};
   hipError_t e = fa::launch_bwd_mfma_sparse(a, elem(dtype),
                                             (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV,
                                             (hipStream_t)stream);

@@ -456,8 +456,18 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   const int N = a.N;
   const int nqb = (N + BR - 1) / BR;
   const BlockPick pk = pick_block(blockIdx.x, gridDim.x, nqb, a.B * a.H, a.causal, DqCfg<D>::MINW);
-  const int bh = pk.bh;
-  const int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;
+  int bh = pk.bh;
+  int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;
+  // Block-sparse by row pieces: the workgroup's item names its row and piece.
+  int piece0 = 0, slot = -1;
+  const bool by_items = SP && a.sq_items != nullptr;
+  if (by_items) {
+    const int* it4 = a.sq_items + 4 * (size_t)blockIdx.x;
+    bh = it4[0];
+    qb = it4[1];
+    piece0 = it4[2];
+    slot = it4[3];
+  }
   const int b = bh / a.H;
 
   const size_t head_off = (size_t)bh * N * D;
@@ -482,19 +492,25 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   int w_tiles = (w_lim + BC - 1) / BC;
 
   // Block-sparse: tile counts and positions j count only the tiles of the
-  // kept key blocks, in increasing order; tile_ix(j) is the key tile.
+  // kept key blocks, in increasing order; tile_ix(j) is the key tile. A row
+  // piece sees the list from its first block on, at most kSparsePiece blocks.
   int n_kept = 0;
+  const unsigned short* plist = blist;
   if constexpr (SP) {
     const int nb = (N + kMaskBlock - 1) / kMaskBlock;
     const unsigned char* mrow = a.bmask + (long long)b * a.bm_sb +
                                 (long long)(bh - b * a.H) * a.bm_sh + (long long)qb * nb;
     n_kept = list_mask_blocks<kBwdThreads>(mrow, 1, 0, min(nb, (kv_lim + kMaskBlock - 1) / kMaskBlock),
                                            blist, bwc);
-    w_tiles = mask_tiles_below(blist, n_kept, w_tiles);
-    ntiles = mask_tiles_below(blist, n_kept, ntiles);
+    if (by_items) {
+      plist = blist + min(piece0, n_kept);
+      n_kept = max(min(n_kept - piece0, kSparsePiece), 0);
+    }
+    w_tiles = mask_tiles_below(plist, n_kept, w_tiles);
+    ntiles = mask_tiles_below(plist, n_kept, ntiles);
   }
   auto tile_ix = [&](int j) -> int {
-    if constexpr (SP) return mask_tile(blist, j);
+    if constexpr (SP) return mask_tile(plist, j);
     else return j;
   };
 
@@ -524,7 +540,8 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   if (my_q < N) {
     const float l = a.lse[(size_t)bh * N + my_q];
     lse2 = (l == -INFINITY) ? 0.f : l * kLog2e;
-    if (hh == 0) a.dsum[(size_t)bh * N + my_q] = dsum;
+    // every piece of a row forms the same D_i; the first one stores it
+    if (hh == 0 && piece0 == 0) a.dsum[(size_t)bh * N + my_q] = dsum;
   }
   const float sl2 = a.scale * kLog2e;
 
@@ -621,7 +638,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   // must not be the last.
   int n_full = a.causal ? (q_blk0 + 1) / BC : ntiles;
   if constexpr (SP) {
-    if (a.causal) n_full = mask_tiles_below(blist, n_kept, n_full);
+    if (a.causal) n_full = mask_tiles_below(plist, n_kept, n_full);
   }
   n_full = min(n_full, ntiles - 1);
   int j = 0;
@@ -632,7 +649,20 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   for (; j < n_full; ++j) tile(j, Full{}, j & 1);
   for (; j < ntiles; ++j) tile(j, Part{}, j & 1);
 
-  if (my_q < N) {
+  if (by_items && slot >= 0) {
+    // fp32 partial dQ of this piece, rows = queries of the block
+    float* dQp = a.sq_part + ((size_t)slot * kMaskBlock + wave * 32 + ql) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = dt * 32 + r4 * 8 + 4 * hh;
+        const f32x16& Q4 = dq[dt];
+        *(f32x4*)(dQp + d0) = f32x4{Q4[4 * r4] * a.scale, Q4[4 * r4 + 1] * a.scale,
+                                    Q4[4 * r4 + 2] * a.scale, Q4[4 * r4 + 3] * a.scale};
+      }
+    }
+  } else if (my_q < N) {
     uint16_t* dQg = (uint16_t*)a.dq + head_off + (size_t)my_q * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -701,6 +731,30 @@ __global__ __launch_bounds__(256) void sparse_dkv_reduce_kernel(BwdArgs a) {
   *(u32x2*)((uint16_t*)a.dv + off) = u32x2{Mfma<T>::pack(sv[0], sv[1]), Mfma<T>::pack(sv[2], sv[3])};
 }
 
+// dQ of the block-sparse rows cut into pieces: the pieces' fp32 partials
+// added in piece order and rounded once.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void sparse_dq_reduce_kernel(BwdArgs a) {
+  constexpr int ROWS = 256 * 4 / D;
+  const int row = blockIdx.x / (kMaskBlock / ROWS);
+  const int r0 = (blockIdx.x % (kMaskBlock / ROWS)) * ROWS;
+  const int* c4 = a.sq_rows + 4 * (size_t)row;
+  const int bh = c4[0], qb = c4[1], slot0 = c4[2], np = c4[3];
+  const int e = threadIdx.x * 4;
+  const int r = r0 + e / D, d0 = e % D;
+  const int q = qb * kMaskBlock + r;
+  if (q >= a.N) return;
+  const size_t blk = (size_t)kMaskBlock * D;
+  const float* p = a.sq_part + (size_t)slot0 * blk + (size_t)r * D + d0;
+  f32x4 acc = *(const f32x4*)p;
+  for (int i = 1; i < np; ++i) {
+    const f32x4 x = *(const f32x4*)(p + i * blk);
+    acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
+  }
+  *(u32x2*)((uint16_t*)a.dq + ((size_t)bh * a.N + q) * D + d0) =
+      u32x2{Mfma<T>::pack(acc[0], acc[1]), Mfma<T>::pack(acc[2], acc[3])};
+}
+
 template <typename T, int D, bool SP = false>
 hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   hipError_t e = hipSuccess;
@@ -713,9 +767,15 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   }
   if (stages & (int)BwdStage::DQ) {
     const long nqb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-    hipLaunchKernelGGL((dq_kernel<T, D, SP>), dim3((unsigned)((long)a.B * a.H * nqb)),
-                       dim3(kBwdThreads), 0, st, a);
+    const long grid = (SP && a.sq_items) ? (long)a.sq_nitems : (long)a.B * a.H * nqb;
+    hipLaunchKernelGGL((dq_kernel<T, D, SP>), dim3((unsigned)grid), dim3(kBwdThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (SP && a.sq_items && a.sq_nrows > 0) {
+      hipLaunchKernelGGL((sparse_dq_reduce_kernel<T, D>),
+                         dim3((unsigned)((long)a.sq_nrows * (kMaskBlock / (256 * 4 / D)))), dim3(256),
+                         0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   if (stages & (int)BwdStage::DKDV) {
     const long nkb = (a.N + 32 * kBwdWaves - 1) / (32 * kBwdWaves);

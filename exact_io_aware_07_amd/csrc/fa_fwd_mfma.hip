@@ -103,8 +103,18 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   const int split = GEN ? blockIdx.x / per_split : 0;
   const BlockPick pk = pick_block(blockIdx.x - split * per_split, per_split, nqb, a.B * a.H, a.causal,
                                   FwdTile<D>::OCC);
-  const int bh = pk.bh;
-  const int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;  // causal: last block has most work
+  int bh = pk.bh;
+  int qb = a.causal ? nqb - 1 - pk.rank : pk.rank;  // causal: last block has most work
+  // Block-sparse by pieces: the workgroup's item names its row and piece.
+  int piece0 = 0, slot = -1;
+  const bool by_items = SP && a.sp_items != nullptr;
+  if (by_items) {
+    const int* it4 = a.sp_items + 4 * (size_t)blockIdx.x;
+    bh = it4[0];
+    qb = it4[1];
+    piece0 = it4[2];
+    slot = it4[3];
+  }
   const int b = bh / a.H;
 
   const size_t head_off = (size_t)bh * N * D;          // Q and O
@@ -138,18 +148,26 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
 
   // Block-sparse: from here on a tile count or position t counts only the
   // tiles of kept blocks, in increasing order; tile_ix(t) is the key tile.
+  // A piece sees the list from its first block on, at most kSparsePiece
+  // blocks of it (the entries after a piece are real blocks or the list's
+  // own end copies, so a prefetch past the piece reads a tile of the head).
   int n_kept = 0;
+  const unsigned short* plist = blist;
   if constexpr (SP) {
     const int nb = (N + kMaskBlock - 1) / kMaskBlock;
     const unsigned char* mrow = a.bmask + (long long)b * a.bm_sb +
                                 (long long)(bh - b * a.H) * a.bm_sh + (long long)qb * nb;
     n_kept = list_mask_blocks<kThreads>(mrow, 1, 0, min(nb, (kv_lim + kMaskBlock - 1) / kMaskBlock),
                                         blist, bwc);
-    w_tiles = mask_tiles_below(blist, n_kept, w_tiles);
-    ntiles = mask_tiles_below(blist, n_kept, ntiles);
+    if (by_items) {
+      plist = blist + min(piece0, n_kept);
+      n_kept = max(min(n_kept - piece0, kSparsePiece), 0);
+    }
+    w_tiles = mask_tiles_below(plist, n_kept, w_tiles);
+    ntiles = mask_tiles_below(plist, n_kept, ntiles);
   }
   auto tile_ix = [&](int t) -> int {
-    if constexpr (SP) return mask_tile(blist, t);
+    if constexpr (SP) return mask_tile(plist, t);
     else return jb + t;
   };
 
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   // further tile, form the branch-free main loop (an even count, so the two
   // S arrays swap roles without copies).
   int n_vis = (a.causal ? min(kv_end, q_blk0 + delta + 1) : kv_end) / BC - jb;
-  if constexpr (SP) n_vis = mask_tiles_below(blist, n_kept, n_vis);
+  if constexpr (SP) n_vis = mask_tiles_below(plist, n_kept, n_vis);
   const int n_full = max(min(n_vis, ntiles - 1), 0) & ~1;
   int j = 0;
   for (; j < n_full; j += 2) {
@@ -323,7 +341,24 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
 
   const float l_tot = halves_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (my_q < N) {
+  if (by_items && slot >= 0) {
+    // the piece's fp32 O (normalised over its keys) and LSE, rows = queries
+    // of the block; the merge combines a row's pieces
+    const int r = wave * 32 + ql;
+    float* Op = a.sp_part + ((size_t)slot * kMaskBlock + r) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = dt * 32 + r4 * 8 + 4 * hh;
+        *(f32x4*)(Op + d0) = f32x4{oacc[dt][4 * r4] * inv, oacc[dt][4 * r4 + 1] * inv,
+                                   oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv};
+      }
+    }
+    if (hh == 0)
+      a.sp_part[(size_t)a.sp_nslots * kMaskBlock * D + (size_t)slot * kMaskBlock + r] =
+          (l_tot > 0.f) ? m_ref * a.scale + fast_log2(l_tot) * kLn2 : -INFINITY;
+  } else if (my_q < N) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -347,8 +382,59 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   }
 }
 
+// O and LSE of the block-sparse rows cut into pieces: the pieces' (O, LSE)
+// combined by the online-softmax rule, m = max LSE_p, w_p = exp(LSE_p - m),
+// O = sum w_p O_p / sum w_p, LSE = m + ln sum w_p (pieces in order). One
+// workgroup per (row, 256 * 4 / D query rows); thread t covers 4 elements.
+template <typename OutT, int D>
+__global__ __launch_bounds__(256) void sparse_o_merge_kernel(FwdArgs a) {
+  constexpr int ROWS = 256 * 4 / D;
+  const int row = blockIdx.x / (kMaskBlock / ROWS);
+  const int r0 = (blockIdx.x % (kMaskBlock / ROWS)) * ROWS;
+  const int* c4 = a.sp_rows + 4 * (size_t)row;
+  const int bh = c4[0], qb = c4[1], slot0 = c4[2], np = c4[3];
+  const int e = threadIdx.x * 4;
+  const int r = r0 + e / D, d0 = e % D;
+  const int q = qb * kMaskBlock + r;
+  if (q >= a.N) return;
+  const size_t blk = (size_t)kMaskBlock * D;
+  const float* lse = a.sp_part + (size_t)a.sp_nslots * blk + (size_t)slot0 * kMaskBlock + r;
+  float m = -INFINITY;
+  for (int i = 0; i < np; ++i) m = fmaxf(m, lse[i * kMaskBlock]);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (m != -INFINITY) {
+    const float* op = a.sp_part + (size_t)slot0 * blk + (size_t)r * D + d0;
+    for (int i = 0; i < np; ++i) {
+      const float w = fast_exp2((lse[i * kMaskBlock] - m) * kLog2e);
+      const f32x4 x = *(const f32x4*)(op + i * blk);
+      acc[0] += w * x[0]; acc[1] += w * x[1]; acc[2] += w * x[2]; acc[3] += w * x[3];
+      den += w;
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const size_t off = ((size_t)bh * a.N + q) * D + d0;
+  if constexpr (std::is_same<OutT, float>::value) {
+    *(f32x4*)((float*)a.o + off) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  } else {
+    *(u32x2*)((uint16_t*)a.o + off) = u32x2{Mfma<OutT>::pack(acc[0] * inv, acc[1] * inv),
+                                            Mfma<OutT>::pack(acc[2] * inv, acc[3] * inv)};
+  }
+  if (d0 == 0) a.lse[(size_t)bh * a.N + q] = den > 0.f ? m + fast_log2(den) * kLn2 : -INFINITY;
+}
+
 template <typename T, int D, bool OF, bool GEN, bool SP = false>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
+  if (SP && a.sp_items) {
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, OF, GEN, SP>), dim3((unsigned)a.sp_nitems), dim3(kThreads),
+                       0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.sp_nrows == 0) return e;
+    const dim3 g((unsigned)((long)a.sp_nrows * (kMaskBlock / (256 * 4 / D))));
+    if (OF) hipLaunchKernelGGL((sparse_o_merge_kernel<float, D>), g, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((sparse_o_merge_kernel<T, D>), g, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const long nqb = (a.N + kBR - 1) / kBR;
   const long total = (long)a.B * a.H * nqb * (GEN ? a.nsplit : 1);
   hipLaunchKernelGGL((fwd_mfma_kernel<T, D, OF, GEN, SP>), dim3((unsigned)total), dim3(kThreads), 0,

@@ -36,6 +36,17 @@ struct FwdArgs {
   // ceil(N / kMaskBlock); nonzero keeps query block i against key block j.
   const unsigned char* bmask;
   long long bm_sb, bm_sh;
+  // Block-sparse by pieces (sp_items != nullptr): workgroup i runs row item
+  // sp_items[4i .. 4i+3] = (b*H + h, query block, first listed key block,
+  // slot), i.e. the kept key blocks at list positions [first, first +
+  // kSparsePiece) of that query block's mask row; slot < 0 writes O and
+  // LSE, slot >= 0 writes the piece's fp32 O [slot][kMaskBlock][d] and LSE
+  // [slot][kMaskBlock] (after all O parts) to sp_part, merged per row
+  // (sp_rows[4r .. 4r+3] = (b*H + h, query block, first slot, pieces)).
+  const int* sp_items;
+  const int* sp_rows;
+  int sp_nitems, sp_nrows, sp_nslots;
+  float* sp_part;
 };
 
 struct BwdArgs {
@@ -75,9 +86,16 @@ struct BwdArgs {
   const int* sp_items;
   const int* sp_cols;
   int sp_nitems, sp_ncols, sp_nslots;
+  // Block-sparse dQ by row pieces, as the forward's (FwdArgs::sp_*): slot
+  // >= 0 writes fp32 partial dQ [slot][kMaskBlock][d] to sq_part, added per
+  // row by the reduction (sq_rows).
+  const int* sq_items;
+  const int* sq_rows;
+  int sq_nitems, sq_nrows, sq_nslots;
+  float* sq_part;
 };
 
-// Kept query blocks per piece of a block-sparse dK/dV column.
+// Blocks per piece of a block-sparse mask row or column.
 constexpr int kSparsePiece = 8;
 
 // Query-head split of the grouped dK/dV stage for a shape: the smallest

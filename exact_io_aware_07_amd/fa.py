@@ -21,7 +21,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0,
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_dsum", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_partial", "fa_merge", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split", "fa_fwd_gqa", "fa_bwd_gqa_workspace_bytes", "fa_bwd_gqa",
-           "fa_fwd_sparse", "fa_bwd_sparse", "fa_sparse_bwd_plan",
+           "fa_fwd_sparse", "fa_bwd_sparse", "fa_sparse_plan",
+           "fa_fwd_sparse_planned_workspace_bytes", "fa_fwd_sparse_planned",
            "fa_bwd_sparse_planned_workspace_bytes", "fa_bwd_sparse_planned", "fa_fp8_quantize", "fa_fwd_fp8",
            "fa_fwd_fp8_workspace_bytes", "fa_fwd_fp8_incoherent", "fa_strerror")
 
@@ -77,13 +78,17 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, ll,
                                 ll, vp, sz, vp, i]
     L.fa_bwd_sparse.restype = i
-    ip = ctypes.POINTER(ctypes.c_int)
-    L.fa_sparse_bwd_plan.argtypes = [vp, ll, ll, i, i, i, i, vp, i, vp, i, ip, ip, ip]
-    L.fa_sparse_bwd_plan.restype = i
-    L.fa_bwd_sparse_planned_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_sparse_plan.argtypes = [vp, ll, ll, i, i, i, i, vp, ll, vp]
+    L.fa_sparse_plan.restype = i
+    L.fa_fwd_sparse_planned_workspace_bytes.argtypes = [i, i, i, i, vp]
+    L.fa_fwd_sparse_planned_workspace_bytes.restype = sz
+    L.fa_fwd_sparse_planned.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, ll, ll, vp, vp,
+                                        vp, sz, vp, i, i]
+    L.fa_fwd_sparse_planned.restype = i
+    L.fa_bwd_sparse_planned_workspace_bytes.argtypes = [i, i, i, i, vp]
     L.fa_bwd_sparse_planned_workspace_bytes.restype = sz
-    L.fa_bwd_sparse_planned.argtypes = ([vp] * 9 + [i, i, i, i, f, i, vp, vp, ll, ll, vp, i, vp, i, i,
-                                                     vp, sz, vp, i])
+    L.fa_bwd_sparse_planned.argtypes = ([vp] * 9 + [i, i, i, i, f, i, vp, vp, ll, ll, vp, vp, vp, sz,
+                                                     vp, i])
     L.fa_bwd_sparse_planned.restype = i
     L.fa_fp8_quantize.argtypes = [vp] * 11 + [i, i, i, i, vp, i]
     L.fa_fp8_quantize.restype = i
@@ -407,57 +412,98 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, block_mask, scale: float,
         raise FaError(st, "fa_bwd_sparse")
 
 
-def fa_sparse_bwd_plan(block_mask, B: int, H: int, N: int, causal: bool = False) -> dict:
-    """Host-side plan of the block-sparse backward (see include/fa.h) from a
-    CPU uint8 block mask of the shapes fa_fwd_sparse accepts. Returns
-    {"items": int32 [n, 4], "cols": int32 [m, 4], "n_slots": s} on the CPU;
-    copy items and cols to the device for fa_bwd_sparse_planned."""
+def fa_sparse_plan(block_mask, B: int, H: int, N: int, causal: bool = False) -> dict:
+    """Host-side plan of the planned block-sparse entry points (see
+    include/fa.h) from a CPU uint8 block mask of the shapes fa_fwd_sparse
+    accepts. Returns, on the CPU, {"plan": int32 flat array, "counts": int32
+    [8]} and views of the plan's four parts as [n, 4] arrays: "col_items",
+    "cols", "row_items", "rows"."""
     if block_mask.is_cuda or block_mask.dtype != torch.uint8:
         raise ValueError("the plan reads a CPU uint8 copy of the mask")
     m = block_mask.contiguous()
     sb, sh = _mask_strides(m, B, H, N, device_ok=False)
-    ni, nc, ns = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    counts = torch.zeros(8, dtype=torch.int32)
     L = lib()
-    st = L.fa_sparse_bwd_plan(_ptr(m), sb, sh, B, H, N, int(bool(causal)), None, 0, None, 0,
-                              ctypes.byref(ni), ctypes.byref(nc), ctypes.byref(ns))
+    st = L.fa_sparse_plan(_ptr(m), sb, sh, B, H, N, int(bool(causal)), None, 0, _ptr(counts))
     if st != FA_OK:
-        raise FaError(st, "fa_sparse_bwd_plan")
-    items = torch.zeros((max(ni.value, 1), 4), dtype=torch.int32)
-    cols = torch.zeros((max(nc.value, 1), 4), dtype=torch.int32)
-    st = L.fa_sparse_bwd_plan(_ptr(m), sb, sh, B, H, N, int(bool(causal)), _ptr(items), items.shape[0],
-                              _ptr(cols), cols.shape[0], ctypes.byref(ni), ctypes.byref(nc),
-                              ctypes.byref(ns))
+        raise FaError(st, "fa_sparse_plan")
+    c = [int(x) for x in counts]
+    n = 4 * (c[0] + c[1] + c[3] + c[4])
+    plan = torch.zeros(max(n, 4), dtype=torch.int32)
+    st = L.fa_sparse_plan(_ptr(m), sb, sh, B, H, N, int(bool(causal)), _ptr(plan), plan.numel(),
+                          _ptr(counts))
     if st != FA_OK:
-        raise FaError(st, "fa_sparse_bwd_plan")
-    return {"items": items[:ni.value], "cols": cols[:nc.value], "n_slots": ns.value}
+        raise FaError(st, "fa_sparse_plan")
+    out = {"plan": plan, "counts": counts}
+    o = 0
+    for name, k in (("col_items", c[0]), ("cols", c[1]), ("row_items", c[3]), ("rows", c[4])):
+        out[name] = plan[o:o + 4 * k].view(k, 4)
+        o += 4 * k
+    return out
 
 
-def fa_bwd_sparse_planned_workspace_bytes(B: int, H: int, N: int, d: int, n_slots: int) -> int:
-    return int(lib().fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, n_slots))
+def fa_fwd_sparse_planned_workspace_bytes(B: int, H: int, N: int, d: int, counts) -> int:
+    c = torch.as_tensor(counts, dtype=torch.int32).contiguous()
+    return int(lib().fa_fwd_sparse_planned_workspace_bytes(B, H, N, d, _ptr(c)))
+
+
+def fa_bwd_sparse_planned_workspace_bytes(B: int, H: int, N: int, d: int, counts) -> int:
+    c = torch.as_tensor(counts, dtype=torch.int32).contiguous()
+    return int(lib().fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, _ptr(c)))
+
+
+def _plan_args(plan: dict, device):
+    """(device plan, CPU counts) of a plan from fa_sparse_plan."""
+    counts = torch.as_tensor(plan["counts"], dtype=torch.int32).contiguous()
+    if counts.is_cuda or counts.numel() != 8:
+        raise ValueError("plan['counts'] must be the 8 host counts of fa_sparse_plan")
+    return plan["plan"].to(device=device, dtype=torch.int32).contiguous(), counts
+
+
+def fa_fwd_sparse_planned(q, k, v, o, lse, block_mask, plan: dict, scale: float, causal: bool = False,
+                          kv_len=None, workspace=None, stream=None) -> None:
+    """fa_fwd_sparse with the plan of fa_sparse_plan (long mask rows cut into
+    pieces whose partial O and LSE are merged)."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("o", o, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    sb, sh = _mask_strides(block_mask, B, H, N)
+    dplan, counts = _plan_args(plan, q.device)
+    need = fa_fwd_sparse_planned_workspace_bytes(B, H, N, d, counts)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_fwd_sparse_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                     float(scale), int(bool(causal)), _kv(kv_len, B), _ptr(block_mask),
+                                     sb, sh, _ptr(dplan), _ptr(counts), _ptr(workspace), ws_bytes,
+                                     _stream(stream, q.device), _DTYPE.get(q.dtype, -99),
+                                     _DTYPE.get(o.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_sparse_planned")
 
 
 def fa_bwd_sparse_planned(q, k, v, o, dout, lse, dq, dk, dv, block_mask, plan: dict, scale: float,
                           causal: bool = False, kv_len=None, workspace=None, stream=None) -> None:
-    """fa_bwd_sparse with the plan of fa_sparse_bwd_plan (its items and cols
-    as device int32 tensors, or CPU ones that are copied here)."""
+    """fa_bwd_sparse with the plan of fa_sparse_plan (long mask columns and
+    rows cut into pieces whose fp32 partials are added in order)."""
     B, H, N, d = q.shape
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype)
     _check_tensor("q", q, q.shape)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     sb, sh = _mask_strides(block_mask, B, H, N)
-    items = plan["items"].to(q.device).contiguous()
-    cols = plan["cols"].to(q.device).contiguous()
-    ns = int(plan["n_slots"])
-    need = fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, ns)
+    dplan, counts = _plan_args(plan, q.device)
+    need = fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, counts)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().fa_bwd_sparse_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
                                      int(bool(causal)), _kv(kv_len, B), _ptr(block_mask), sb, sh,
-                                     _ptr(items), items.shape[0], _ptr(cols) if cols.numel() else None,
-                                     cols.shape[0], ns, _ptr(workspace), ws_bytes,
+                                     _ptr(dplan), _ptr(counts), _ptr(workspace), ws_bytes,
                                      _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_sparse_planned")

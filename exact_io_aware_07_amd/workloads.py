@@ -119,6 +119,14 @@ SPARSE = Workload("long_block_sparse_band_bf16_fwd_bwd", 1, 16, 16384, 64, "bf16
                   backward=True, measurement_only=True, block_pattern="band_sink",
                   note="B=1 H=16 N=16384 d=64 bf16, 128x128 block mask: band of 3 + first block")
 
+# The same shape with a global first block: it keeps every key block and
+# every query block keeps it, so one mask row and one mask column hold 128
+# kept blocks while the others hold four (the load the plan's pieces spread).
+SPARSE_GLOBAL = Workload("long_block_sparse_global_bf16_fwd_bwd", 1, 16, 16384, 64, "bf16",
+                         backward=True, measurement_only=True, block_pattern="band_global",
+                         note="B=1 H=16 N=16384 d=64 bf16, 128x128 block mask: band of 3 + "
+                              "global first block (its row and column kept)")
+
 # FP8 forward: the long-context shape with four outlier channels of Q and K
 # (x16, the same channels in Q and K of a head), the case the rotation of
 # the FP8 path is for.
@@ -128,7 +136,7 @@ FP8 = Workload("long_context_fp8_outlier_channels_fwd", 1, 32, 4096, 128, "bf16"
 
 CONFIGS: Dict[str, Workload] = {w.name: w for w in (TINY, BERT, LONG, TRADE, GPT2)}
 MEASUREMENT: Dict[str, Workload] = {w.name: w for w in (LONG_BWD, TRADE_BWD, FEW_HEADS, GQA, SPARSE,
-                                                        FP8)}
+                                                        SPARSE_GLOBAL, FP8)}
 ALL: Dict[str, Workload] = {**CONFIGS, **MEASUREMENT}
 
 
@@ -217,6 +225,7 @@ def block_mask(w: Workload) -> Optional[torch.Tensor]:
     ceil(N / 128)), shared by every batch and head, or None for a dense one.
 
     "band_sink": query block i keeps key blocks i - 1, i, i + 1 and 0.
+    "band_global": the same, and query block 0 keeps every key block.
     """
     if w.block_pattern is None:
         return None
@@ -225,6 +234,8 @@ def block_mask(w: Workload) -> Optional[torch.Tensor]:
     j = torch.arange(nb)[None, :]
     if w.block_pattern == "band_sink":
         return (((i - j).abs() <= 1) | (j == 0)).to(torch.uint8)
+    if w.block_pattern == "band_global":
+        return (((i - j).abs() <= 1) | (j == 0) | (i == 0)).to(torch.uint8)
     raise ValueError(f"unknown block pattern {w.block_pattern!r}")
 
 

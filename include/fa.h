@@ -243,40 +243,54 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o,
                   size_t workspace_bytes, void* stream, int dtype);
 
 /*
- * Block-sparse backward with long mask columns cut into pieces. In
- * fa_bwd_sparse one workgroup computes a key block's dK, dV over every kept
- * query block of its mask column, so a column kept by many query blocks
- * (a global key, the first block of a sink pattern) is one long serial job.
- * fa_sparse_bwd_plan reads a HOST copy of the mask (same layout and
- * strides as the device mask) and cuts every column with more than 8 kept
- * query blocks (causal: blocks on or after the diagonal) into pieces of at
- * most 8, longest first. fa_bwd_sparse_planned runs one workgroup per piece:
- * pieces of a cut column write fp32 partial dK, dV to the workspace and a
- * second launch adds them in piece order (deterministic); other columns
- * are written as in fa_bwd_sparse, bit for bit.
- *   fa_sparse_bwd_plan: counts in *n_items, *n_cols, *n_slots; with items
- *   and cols NULL only the counts; else items (int32 [n_items][4]) and cols
- *   (int32 [n_cols][4]) are filled (FA_ERR_INVALID_ARG if a capacity, in
- *   entries of 4 ints, is too small). Host memory only, no HIP call.
- *   fa_bwd_sparse_planned: the arguments of fa_bwd_sparse plus the plan
- *   copied to device memory (items, cols: 4-byte aligned) and its three
- *   counts; workspace of fa_bwd_sparse_planned_workspace_bytes(B, H, N, d,
- *   n_slots) bytes. The plan must come from the same mask, strides, B, H,
- *   N and causal: it is not checked on the device.
+ * Block-sparse attention with long mask lines cut into pieces. In
+ * fa_fwd_sparse one workgroup computes a query block over every kept key
+ * block of its mask row, and in fa_bwd_sparse one workgroup computes a key
+ * block's dK, dV over every kept query block of its mask column (and one a
+ * query block's dQ over its row), so a line with many kept blocks (a global
+ * token, the first block of a sink pattern) is one long serial job.
+ * fa_sparse_plan reads a HOST copy of the mask (same layout and strides as
+ * the device mask) and cuts every line with more than 8 kept blocks into
+ * pieces of at most 8, longest first: columns count the query blocks from
+ * the diagonal on when causal, rows the key blocks up to the diagonal.
+ * The planned entry points run one workgroup per piece; pieces of a cut
+ * line write fp32 partial results to the workspace and a second launch
+ * combines them in piece order (deterministic): partial O with its LSE for
+ * the forward (rescaled to the common maximum, the online-softmax merge),
+ * partial sums for dK, dV and dQ. Lines that are not cut are written as by
+ * fa_fwd_sparse / fa_bwd_sparse, bit for bit.
+ *   fa_sparse_plan: counts[8] = {column items, cut columns, column slots,
+ *   row items, cut rows, row slots, 0, 0}; with plan NULL only the counts,
+ *   else plan (int32, plan_ints entries) holds the column items, the cut
+ *   columns, the row items and the cut rows in that order, 4 ints each
+ *   (FA_ERR_INVALID_ARG if plan_ints is smaller than 4 x the sum of counts
+ *   0, 1, 3, 4). Host memory only, no HIP call.
+ *   fa_fwd_sparse_planned / fa_bwd_sparse_planned: the arguments of
+ *   fa_fwd_sparse / fa_bwd_sparse plus the plan copied to device memory
+ *   (4-byte aligned) and the host array counts; workspace of
+ *   fa_{fwd,bwd}_sparse_planned_workspace_bytes(B, H, N, d, counts) bytes
+ *   (the forward needs none when no row is cut). The plan must come from
+ *   the same mask, strides, B, H, N and causal: it is not checked on the
+ *   device.
  */
-int fa_sparse_bwd_plan(const unsigned char* host_mask, long long mask_stride_b,
-                       long long mask_stride_h, int B, int H, int N, int causal,
-                       int* items, int max_items, int* cols, int max_cols,
-                       int* n_items, int* n_cols, int* n_slots);
-size_t fa_bwd_sparse_planned_workspace_bytes(int B, int H, int N, int d, int n_slots);
+int fa_sparse_plan(const unsigned char* host_mask, long long mask_stride_b,
+                   long long mask_stride_h, int B, int H, int N, int causal, int* plan,
+                   long long plan_ints, int* counts);
+size_t fa_fwd_sparse_planned_workspace_bytes(int B, int H, int N, int d, const int* counts);
+int fa_fwd_sparse_planned(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int causal,
+                          const int* kv_len, const unsigned char* block_mask,
+                          long long mask_stride_b, long long mask_stride_h,
+                          const int* plan, const int* counts, void* workspace,
+                          size_t workspace_bytes, void* stream, int in_dtype, int o_dtype);
+size_t fa_bwd_sparse_planned_workspace_bytes(int B, int H, int N, int d, const int* counts);
 int fa_bwd_sparse_planned(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk,
                           void* dv, int B, int H, int N, int d, float scale, int causal,
                           const int* kv_len, const unsigned char* block_mask,
                           long long mask_stride_b, long long mask_stride_h,
-                          const int* items, int n_items, const int* cols, int n_cols,
-                          int n_slots, void* workspace, size_t workspace_bytes,
-                          void* stream, int dtype);
+                          const int* plan, const int* counts, void* workspace,
+                          size_t workspace_bytes, void* stream, int dtype);
 
 /*
  * FP8 forward with incoherent processing (marketmaker.cc article, section

@@ -381,67 +381,133 @@ def test_fp8_workspace_holds_every_buffer():
     assert need <= got <= need + 7 * 256
 
 
-def _plan_counts(mask, B, H, N, causal):
+def _plan_counts(mask, B, H, N, causal, columns):
+    """Kept blocks per mask line, written out: a column (key block kb) counts
+    query blocks from the diagonal on when causal; a row (query block qb)
+    counts key blocks up to the diagonal."""
     nb = (N + 127) // 128
     m = mask.expand(B, H, nb, nb) if mask.dim() == 2 else mask
     out = {}
     for b in range(B):
         for h in range(H):
-            for kb in range(nb):
-                lo = kb if causal else 0
-                out[(b * H + h, kb)] = int((m[b, h, lo:, kb] != 0).sum())
+            for x in range(nb):
+                if columns:
+                    line = m[b, h, (x if causal else 0):, x]
+                else:
+                    line = m[b, h, x, :(x + 1 if causal else nb)]
+                out[(b * H + h, x)] = int((line != 0).sum())
     return out
 
 
+def _check_pieces(items, lines, counts):
+    """Every line once, whole (first 0, slot -1) when it holds at most 8
+    kept blocks, else in pieces of 8 with consecutive slots named by its
+    cut line; the slots of the cut lines tile [0, total); longest first."""
+    seen = {}
+    for bh, x, first, slot in items:
+        seen.setdefault((bh, x), []).append((first, slot))
+    assert set(seen) == set(counts)
+    cut = {(c[0], c[1]): c for c in lines}
+    sizes = []
+    for key, n in counts.items():
+        got = sorted(seen[key])
+        if n <= 8:
+            assert got == [(0, -1)] and key not in cut
+            sizes.append(n)
+            continue
+        pieces = -(-n // 8)
+        _, _, slot0, np_ = cut[key]
+        assert np_ == pieces and got == [(8 * i, slot0 + i) for i in range(pieces)]
+        sizes += [min(8, n - 8 * i) for i in range(pieces)]
+    spans = sorted((c[2], c[3]) for c in lines)
+    assert [s for s, _ in spans] == [sum(n for _, n in spans[:i]) for i in range(len(spans))]
+    size_of = lambda it: min(8, counts[(it[0], it[1])] - it[2])
+    order = [size_of(it) for it in items]
+    assert order == sorted(order, reverse=True) and sorted(order) == sorted(sizes)
+    return sum(n for _, n in spans)
+
+
 @pytest.mark.parametrize("causal", [False, True])
-def test_sparse_plan_cuts_long_columns_into_pieces_of_eight(causal):
+def test_sparse_plan_cuts_long_lines_into_pieces_of_eight(causal):
     from exact_io_aware_07_amd import workloads as W
     B, H, N = 2, 3, 128 * 40
     mask = W.random_block_mask((B, H), N, 0.45, seed=7)
     mask[0, 1, :, 3] = 1                      # one full column
     mask[1, 2, :, 5] = 0                      # one empty column
-    plan = fa.fa_sparse_bwd_plan(mask, B, H, N, causal)
-    items, cols = plan["items"].tolist(), plan["cols"].tolist()
-    counts = _plan_counts(mask, B, H, N, causal)
-    seen = {}
-    for bh, kb, first, slot in items:
-        seen.setdefault((bh, kb), []).append((first, slot))
-    assert set(seen) == set(counts)           # every key block of every head, once or in pieces
-    col_of = {(c[0], c[1]): c for c in cols}
-    sizes = []
-    for key, n in counts.items():
-        got = sorted(seen[key])
-        if n <= 8:
-            assert got == [(0, -1)] and key not in col_of
-            sizes.append(n)
-            continue
-        pieces = -(-n // 8)
-        bh, kb, slot0, np_ = col_of[key]
-        assert np_ == pieces and got == [(8 * i, slot0 + i) for i in range(pieces)]
-        sizes += [min(8, n - 8 * i) for i in range(pieces)]
-    assert plan["n_slots"] == sum(c[3] for c in cols)
-    assert sorted(c[2] for c in cols) == [sum(x[3] for x in cols if x[2] < c[2]) for c in sorted(cols, key=lambda c: c[2])]
-    # longest pieces first
-    size_of = lambda it: min(8, counts[(it[0], it[1])] - it[2]) if counts[(it[0], it[1])] > 8 else counts[(it[0], it[1])]
-    order = [size_of(it) for it in items]
-    assert order == sorted(order, reverse=True) and sorted(order) == sorted(sizes)
+    mask[1, 0, 30, :] = 1                     # one full row
+    mask[0, 2, 4, :] = 0                      # one empty row
+    plan = fa.fa_sparse_plan(mask, B, H, N, causal)
+    c = plan["counts"].tolist()
+    assert c[6:] == [0, 0] and len(plan["plan"]) >= 4 * (c[0] + c[1] + c[3] + c[4])
+    cols = _check_pieces(plan["col_items"].tolist(), plan["cols"].tolist(),
+                         _plan_counts(mask, B, H, N, causal, True))
+    rows = _check_pieces(plan["row_items"].tolist(), plan["rows"].tolist(),
+                         _plan_counts(mask, B, H, N, causal, False))
+    assert (c[2], c[5]) == (cols, rows) and cols > 0 and rows > 0
+    assert (c[1], c[4]) == (len(plan["cols"]), len(plan["rows"]))
+
+
+def test_sparse_plan_of_a_short_mask_cuts_nothing():
+    mask = torch.ones(8, 8, dtype=torch.uint8)
+    plan = fa.fa_sparse_plan(mask, 2, 3, 1000, False)
+    assert plan["counts"].tolist() == [48, 0, 0, 48, 0, 0, 0, 0]
 
 
 def test_sparse_plan_validation_and_counts_only():
     L = fa.lib()
-    n = [ctypes.c_int(0) for _ in range(3)]
-    r = lambda *a: L.fa_sparse_bwd_plan(*a, *(ctypes.byref(x) for x in n))
-    assert r(None, 0, 0, 1, 1, 300, 0, None, 0, None, 0) == fa.FA_ERR_INVALID_ARG     # mask missing
+    counts = (ctypes.c_int * 8)()
+    r = lambda *a: L.fa_sparse_plan(*a, counts)
+    assert r(None, 0, 0, 1, 1, 300, 0, None, 0) == fa.FA_ERR_INVALID_ARG     # mask missing
     m = (ctypes.c_ubyte * 9)(*([1] * 9))
-    assert r(m, 0, 0, 1, 1, 300, 2, None, 0, None, 0) == fa.FA_ERR_INVALID_ARG        # causal 2
-    assert r(m, -1, 0, 1, 1, 300, 0, None, 0, None, 0) == fa.FA_ERR_INVALID_ARG
-    assert r(m, 0, 0, 1, 1, 300, 0, None, 0, None, 0) == fa.FA_OK
-    assert [x.value for x in n] == [3, 0, 0]
-    items = (ctypes.c_int * 8)()
-    cols = (ctypes.c_int * 4)()
-    assert r(m, 0, 0, 1, 1, 300, 0, items, 2, cols, 1) == fa.FA_ERR_INVALID_ARG       # 3 items, room for 2
-    assert fa.fa_bwd_sparse_planned_workspace_bytes(1, 2, 300, 64, 3) == 2 * 300 * 4 + 2 * 3 * 128 * 64 * 4 + 256 - (2 * 300 * 4) % 256
-    assert L.fa_bwd_sparse_planned(*([A] * 9), 1, 2, 300, 64, 0.125, 0, None, A, 0, 0, A, 2, A, 0, 0,
-                                   A, 1 << 20, None, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG  # 2 items < 3 key blocks
-    assert L.fa_bwd_sparse_planned(*([A] * 9), 1, 2, 300, 64, 0.125, 0, None, A, 0, 0, A, 6, A, 1, 0,
-                                   A, 1 << 20, None, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG  # cols without slots
+    assert r(m, 0, 0, 1, 1, 300, 2, None, 0) == fa.FA_ERR_INVALID_ARG        # causal 2
+    assert r(m, -1, 0, 1, 1, 300, 0, None, 0) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_sparse_plan(m, 0, 0, 1, 1, 300, 0, None, 0, None) == fa.FA_ERR_INVALID_ARG
+    assert r(m, 0, 0, 1, 1, 300, 0, None, 0) == fa.FA_OK
+    assert list(counts) == [3, 0, 0, 3, 0, 0, 0, 0]
+    buf = (ctypes.c_int * 24)()
+    assert r(m, 0, 0, 1, 1, 300, 0, buf, 23) == fa.FA_ERR_INVALID_ARG        # 6 items, room for 5.75
+    assert r(m, 0, 0, 1, 1, 300, 0, buf, 24) == fa.FA_OK
+    assert list(buf) == [0, 0, 0, -1, 0, 1, 0, -1, 0, 2, 0, -1] * 2
+    big = (ctypes.c_ubyte * (4097 * 4097))()
+    assert r(big, 0, 0, 1, 1, 4097 * 128, 0, None, 0) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_sparse_planned_workspace_sizes():
+    c = [3, 1, 5, 3, 1, 4, 0, 0]
+    assert fa.fa_fwd_sparse_planned_workspace_bytes(1, 2, 300, 64, c) == 4 * 128 * 65 * 4
+    assert fa.fa_fwd_sparse_planned_workspace_bytes(1, 2, 300, 64, [3, 0, 0, 3, 0, 0, 0, 0]) == 0
+    dsum = 2 * 300 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert fa.fa_bwd_sparse_planned_workspace_bytes(1, 2, 300, 128, c) == (
+        up(dsum) + up(2 * 5 * 128 * 128 * 4) + 4 * 128 * 128 * 4)
+    assert fa.fa_bwd_sparse_planned_workspace_bytes(1, 2, 300, 96, c) == 0
+
+
+def test_sparse_planned_validation():
+    L = fa.lib()
+    C = lambda *v: (ctypes.c_int * 8)(*v)
+    ok = C(6, 0, 0, 6, 0, 0, 0, 0)               # B=1 H=2 N=300: 6 lines of each kind
+    fwd = lambda counts, ws=1 << 20, **kw: L.fa_fwd_sparse_planned(
+        A, A, A, A, A, 1, 2, 300, 64, 0.125, 0, None, kw.get("mask", A), 0, 0, kw.get("plan", A),
+        counts, A, ws, None, fa.FA_BF16, fa.FA_BF16)
+    bwd = lambda counts, ws=1 << 20, **kw: L.fa_bwd_sparse_planned(
+        *([A] * 9), 1, 2, 300, 64, 0.125, 0, None, kw.get("mask", A), 0, 0, kw.get("plan", A), counts,
+        A, ws, None, fa.FA_BF16)
+    for f in (fwd, bwd):
+        assert f(C(5, 0, 0, 6, 0, 0, 0, 0)) == fa.FA_ERR_INVALID_ARG       # too few column items
+        assert f(C(6, 0, 0, 5, 0, 0, 0, 0)) == fa.FA_ERR_INVALID_ARG       # too few row items
+        assert f(C(7, 1, 0, 6, 0, 0, 0, 0)) == fa.FA_ERR_INVALID_ARG       # cut column without slots
+        assert f(C(6, 0, 0, 7, 0, 2, 0, 0)) == fa.FA_ERR_INVALID_ARG       # slots without a cut row
+        assert f(C(-1, 0, 0, 6, 0, 0, 0, 0)) == fa.FA_ERR_INVALID_ARG
+        assert f(None) == fa.FA_ERR_INVALID_ARG
+        assert f(ok, plan=None) == fa.FA_ERR_INVALID_ARG
+        assert f(ok, plan=A + 2) == fa.FA_ERR_INVALID_ARG                 # misaligned plan
+        assert f(ok, mask=None) == fa.FA_ERR_INVALID_ARG
+    assert fwd(C(6, 0, 0, 7, 1, 2, 0, 0), ws=2 * 128 * 65 * 4 - 1) == fa.FA_ERR_WORKSPACE
+    assert bwd(ok, ws=0) == fa.FA_ERR_WORKSPACE
+    # empty problems need no pointers
+    assert L.fa_fwd_sparse_planned(None, None, None, None, None, 0, 2, 300, 64, 0.125, 0, None, None, 0,
+                                   0, None, C(0, 0, 0, 0, 0, 0, 0, 0), None, 0, None, fa.FA_BF16,
+                                   fa.FA_BF16) == fa.FA_OK
+    assert L.fa_bwd_sparse_planned(*([None] * 9), 1, 2, 0, 64, 0.125, 0, None, None, 0, 0, None,
+                                   C(0, 0, 0, 0, 0, 0, 0, 0), None, 0, None, fa.FA_BF16) == fa.FA_OK

@@ -94,11 +94,13 @@ def test_every_other_entry_point_allocates_nothing():
     its workspace: no torch allocation during the calls and no change in the
     device's free memory (the library never allocates)."""
     from exact_io_aware_07_amd import (fa_bwd_gqa, fa_bwd_gqa_workspace_bytes, fa_bwd_sparse,
+                                       fa_bwd_sparse_planned, fa_bwd_sparse_planned_workspace_bytes,
                                        fa_bwd_workspace_bytes, fa_fwd_fp8_incoherent,
                                        fa_fwd_fp8_workspace_bytes, fa_fwd_gqa, fa_fwd_sparse,
-                                       fa_fwd_split, fa_fwd_split_workspace_bytes)
+                                       fa_fwd_sparse_planned, fa_fwd_sparse_planned_workspace_bytes,
+                                       fa_fwd_split, fa_fwd_split_workspace_bytes, fa_sparse_plan)
     B, H, Hkv, N, d = 2, 8, 2, 2048, 128
-    say("memory of the split, GQA, sparse and FP8 paths")
+    say("memory of the split, GQA, sparse, planned sparse and FP8 paths")
     inp = W.random_case(B, H, N, d, "bf16", seed=30, backward=True)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
     kg, vg = k[:, :Hkv].contiguous(), v[:, :Hkv].contiguous()
@@ -106,10 +108,16 @@ def test_every_other_entry_point_allocates_nothing():
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     dkg, dvg = torch.empty_like(kg), torch.empty_like(vg)
-    mask = W.random_block_mask((), N, 0.5, seed=31).cuda()
+    mask_h = W.random_block_mask((), N, 0.7, seed=31)
+    mask = mask_h.cuda()
+    plan = fa_sparse_plan(mask_h, B, H, N, False)
+    assert plan["counts"][2] > 0 and plan["counts"][5] > 0
+    plan = {"plan": plan["plan"].cuda(), "counts": plan["counts"]}
     signs = W.random_signs(d, seed=32).cuda()
     ws_bytes = max(fa_fwd_split_workspace_bytes(B, H, N, d, 4), fa_bwd_gqa_workspace_bytes(B, H, Hkv, N, d),
-                   fa_bwd_workspace_bytes(B, H, N, d), fa_fwd_fp8_workspace_bytes(B, H, N, d))
+                   fa_bwd_workspace_bytes(B, H, N, d), fa_fwd_fp8_workspace_bytes(B, H, N, d),
+                   fa_fwd_sparse_planned_workspace_bytes(B, H, N, d, plan["counts"]),
+                   fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, plan["counts"]))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
     def calls():
@@ -118,6 +126,8 @@ def test_every_other_entry_point_allocates_nothing():
         fa_bwd_gqa(q, kg, vg, o, do, lse, dq, dkg, dvg, 0.1, True, None, ws)
         fa_fwd_sparse(q, k, v, o, lse, mask, 0.1, False)
         fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, mask, 0.1, False, None, ws)
+        fa_fwd_sparse_planned(q, k, v, o, lse, mask, plan, 0.1, False, None, ws)
+        fa_bwd_sparse_planned(q, k, v, o, do, lse, dq, dk, dv, mask, plan, 0.1, False, None, ws)
         fa_fwd_fp8_incoherent(q, k, v, signs, o, lse, 0.1, False, None, ws)
 
     calls()  # code objects load

@@ -5,7 +5,9 @@ Exact properties checked besides the oracle: a mask that keeps every block
 gives fa_fwd / fa_bwd bit for bit (the kernels then visit the same tiles in
 the same order), and so does a causal mask keeping the blocks on and below
 the diagonal; one mask shared by all heads (stride 0) gives the same bits
-as that mask copied per head.
+as that mask copied per head. The planned entry points (mask lines with
+more than 8 kept blocks cut into pieces) give the bits of the plain sparse
+ones on every line they do not cut, and match the oracle on the cut ones.
 """
 import numpy as np
 import pytest
@@ -165,61 +167,104 @@ def test_measurement_shape_sampled_against_oracle():
         assert e <= GRAD_REL_FRO, (name, e)
 
 
-def planned(inp, mask, scale, causal):
-    """fa_fwd_sparse, then the backward by the host plan of the mask."""
-    from exact_io_aware_07_amd import fa_bwd_sparse_planned, fa_sparse_bwd_plan
+def planned(inp, mask, scale, causal, out_dtype=None, o_bwd=None, lse_bwd=None):
+    """The forward and backward by the host plan of the mask (the backward
+    on o_bwd, lse_bwd when given, else on the planned forward's own)."""
+    from exact_io_aware_07_amd import fa_bwd_sparse_planned, fa_fwd_sparse_planned, fa_sparse_plan
     q, k, v, do, kv = (dev(inp[n]) for n in ("q", "k", "v", "do", "kv_len"))
     B, H, N, d = q.shape
-    plan = fa_sparse_bwd_plan(mask.contiguous(), B, H, N, causal)
+    plan = fa_sparse_plan(mask.contiguous(), B, H, N, causal)
     m = mask.contiguous().cuda()
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device="cuda")
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    fa_fwd_sparse(q, k, v, o, lse, m, scale, causal, kv)
+    fa_fwd_sparse_planned(q, k, v, o, lse, m, plan, scale, causal, kv)
+    if o_bwd is None:
+        o_bwd, lse_bwd = (o if o.dtype == q.dtype else o.to(q.dtype)), lse
     grads = [torch.empty_like(q) for _ in range(3)]
-    fa_bwd_sparse_planned(q, k, v, o, do, lse, *grads, m, plan, scale, causal, kv)
+    fa_bwd_sparse_planned(q, k, v, o_bwd, do, lse_bwd, *grads, m, plan, scale, causal, kv)
     torch.cuda.synchronize()
     return o, lse, grads, plan
 
 
+def cut_lines(plan, key, B, H, N):
+    """bool [B, H, N] of the queries (key "rows") or keys ("cols") in mask
+    lines the plan cut into pieces."""
+    cut = torch.zeros(B * H, N, dtype=torch.bool)
+    for bh, blk, _, _ in plan[key].tolist():
+        cut[bh, blk * 128:(blk + 1) * 128] = True
+    return cut.view(B, H, N)
+
+
 @pytest.mark.parametrize("causal", [False, True])
-def test_planned_backward_without_long_columns_is_the_same_bits(causal):
-    B, H, N, d = 2, 2, 1000, 64       # 8 blocks: no column holds more than 8
-    say(f"sparse planned, no cut column, causal={causal}")
+def test_planned_without_long_lines_is_the_same_bits(causal):
+    B, H, N, d = 2, 2, 1000, 64       # 8 blocks: no line holds more than 8
+    say(f"sparse planned, nothing cut, causal={causal}")
     inp = W.random_case(B, H, N, d, "bf16", seed=40, causal=causal, backward=True)
     mask = W.random_block_mask((B, H), N, 0.7, seed=41)
-    _, _, g1, plan = planned(inp, mask, d ** -0.5, causal)
-    assert plan["n_slots"] == 0
-    _, _, g2 = run(inp, mask, d ** -0.5, causal)
+    o1, l1, g1, plan = planned(inp, mask, d ** -0.5, causal)
+    c = plan["counts"].tolist()
+    assert c[2] == 0 and c[5] == 0
+    o2, l2, g2 = run(inp, mask, d ** -0.5, causal)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-def test_planned_backward_with_long_columns_matches_oracle(d, causal):
+def test_planned_with_long_lines_matches_oracle(d, causal):
+    """Cut rows and columns against the oracle; the lines not cut give the
+    bits of fa_fwd_sparse / fa_bwd_sparse (the backward run on one O, LSE)."""
     B, H, N = 1, 2, 2100                 # 17 blocks
-    say(f"sparse planned, cut columns d={d} causal={causal}")
-    inp = W.random_case(B, H, N, d, "bf16", seed=42 + d, causal=causal, backward=True, kv_len=[1900])
-    mask = W.random_block_mask((B, H), N, 0.6, seed=43)
+    kv = [1900]
+    say(f"sparse planned, cut rows and columns d={d} causal={causal}")
+    inp = W.random_case(B, H, N, d, "bf16", seed=42 + d, causal=causal, backward=True, kv_len=kv)
+    mask = W.random_block_mask((B, H), N, 0.4, seed=43)
     mask[0, 0, :, 0] = 1
     mask[0, 1, :, 2] = 1
-    o, lse, grads, plan = planned(inp, mask, d ** -0.5, causal)
-    assert plan["n_slots"] > 0
-    ref = attn_bwd64_sparse(inp["q"], inp["k"], inp["v"], inp["do"], d ** -0.5, causal, [1900], mask.numpy())
+    mask[0, 0, 16, :] = 1
+    mask[0, 1, 12, :] = 1
+    o, lse, grads, plan = planned(inp, mask, d ** -0.5, causal, out_dtype=torch.float32)
+    c = plan["counts"].tolist()
+    assert c[2] > 0 and c[5] > 0
+    o_ref, lse_ref = attn_fwd64_sparse(inp["q"], inp["k"], inp["v"], d ** -0.5, causal, kv, mask.numpy())
+    check_fwd(o, lse, o_ref, lse_ref)
+    ref = attn_bwd64_sparse(inp["q"], inp["k"], inp["v"], inp["do"], d ** -0.5, causal, kv, mask.numpy())
     check_grads(grads, ref, f"planned d={d}")
-    _, _, g2 = run(inp, mask, d ** -0.5, causal)
-    for a, b in zip(grads, g2):  # same gradients, other summation order where cut
+    # bits of the lines not cut, both passes on the plain sparse forward's O
+    o2, l2, g2 = run(inp, mask, d ** -0.5, causal)
+    o3, l3, g3, _ = planned(inp, mask, d ** -0.5, causal, o_bwd=o2, lse_bwd=l2)
+    rows = cut_lines(plan, "rows", B, H, N).cuda()
+    cols = cut_lines(plan, "cols", B, H, N).cuda()
+    assert rows.any() and (~rows).any() and cols.any() and (~cols).any()
+    assert torch.equal(o3[~rows], o2[~rows]) and torch.equal(l3[~rows], l2[~rows])
+    assert torch.equal(g3[0][~rows], g2[0][~rows])
+    assert torch.equal(g3[1][~cols], g2[1][~cols]) and torch.equal(g3[2][~cols], g2[2][~cols])
+    fin = torch.isfinite(l2)
+    assert torch.allclose(l3[fin], l2[fin], atol=1e-5, rtol=0)
+    assert rel_fro(np64(o3), np64(o2)) < 5e-3
+    for a, b in zip(g3, g2):          # same gradients, other summation order where cut
         assert rel_fro(np64(a), np64(b)) < 5e-3
 
 
-def test_planned_backward_measurement_shape_sampled_against_oracle():
-    w = W.SPARSE
+@pytest.mark.parametrize("wname", ["SPARSE", "SPARSE_GLOBAL"])
+def test_planned_measurement_shapes_sampled_against_oracle(wname):
+    w = getattr(W, wname)
     say(f"sparse planned full size {w.name}")
     inp = W.make_inputs(w, seed=0)
     mask = W.block_mask(w)
-    _, _, grads, plan = planned(inp, mask, w.scale, w.causal)
-    assert plan["n_slots"] == w.H * 16      # the first key block, kept by all 128 query blocks
+    o, lse, grads, plan = planned(inp, mask, w.scale, w.causal, out_dtype=torch.float32)
+    c = plan["counts"].tolist()
+    # the first key block is kept by all 128 query blocks (16 pieces a head);
+    # with the global pattern the first query block also keeps all 128
+    assert c[2] == w.H * 16 and c[5] == (w.H * 16 if wname == "SPARSE_GLOBAL" else 0)
     rows = [0, 1, 127, 128, 129, 5000, 8191, 8192, 16000, w.N - 1]
+    for h in (0, w.H - 1):
+        o_ref, lse_ref = attn_fwd64_sparse(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1],
+                                           inp["v"][:, h:h + 1], w.scale, w.causal, None,
+                                           mask.numpy(), rows=rows)
+        st = fwd_stats(np64(o[:, h:h + 1, rows]), np64(lse[:, h:h + 1, rows]), o_ref, lse_ref)
+        assert st["max_abs"] <= FWD_MAX_ABS and st["lse_max_abs"] <= LSE_MAX_ABS, st
     h = 11
     sq, sk, sv = attn_bwd64_sparse_sampled(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.causal,
                                            None, mask.numpy(), [(0, h)], rows, rows)
@@ -227,5 +272,5 @@ def test_planned_backward_measurement_shape_sampled_against_oracle():
     for name, got, ref in (("dq", dq[0, h, rows], sq[0]), ("dk", dk[0, h, rows], sk[0]),
                            ("dv", dv[0, h, rows], sv[0])):
         e = rel_fro(np64(got), ref)
-        print(f"planned full size {name} rel-fro {e:.2e}", flush=True)
+        print(f"planned full size {wname} {name} rel-fro {e:.2e}", flush=True)
         assert e <= GRAD_REL_FRO, (name, e)
