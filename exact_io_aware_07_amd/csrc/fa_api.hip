@@ -434,6 +434,21 @@ void sparse_pieces(const unsigned char* host_mask, long long sb, long long sh, i
   }
   std::stable_sort(its.begin(), its.end(),
                    [](const SparseItem& p, const SparseItem& q) { return p.size > q.size; });
+  // Workgroup i runs on XCD i % 8: deal the items so that every item of head
+  // bh sits at a position of class bh % 8, and the head's tiles share one
+  // L2, keeping longest first within a class; once a class runs out, its
+  // positions take items of the class with the most left.
+  std::vector<SparseItem> cls[8];
+  for (const auto& it : its) cls[it.bh % 8].push_back(it);
+  size_t pos[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (size_t p = 0; p < its.size(); ++p) {
+    int x = (int)(p % 8);
+    if (pos[x] == cls[x].size()) {
+      for (int y = 0; y < 8; ++y)
+        if (cls[y].size() - pos[y] > cls[x].size() - pos[x]) x = y;
+    }
+    its[p] = cls[x][pos[x]++];
+  }
 }
 
 // Host checks shared by the planned entry points; plan offsets in ints.

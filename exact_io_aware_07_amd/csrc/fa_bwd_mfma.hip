@@ -704,11 +704,12 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(const float* __restrict
 }
 
 // dK, dV of the block-sparse columns cut into pieces: the sum of each
-// column's fp32 piece partials, in piece order, rounded once. One workgroup
-// per (column, 32 key rows); thread t covers 4 consecutive elements.
+// column's fp32 piece partials, in piece order, rounded once. One wave per
+// (column, 256 / D key rows), so that even a few cut columns spread over
+// the chip; thread t covers 4 consecutive elements.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void sparse_dkv_reduce_kernel(BwdArgs a) {
-  constexpr int ROWS = 256 * 4 / D;  // key rows per workgroup (16 or 8)
+__global__ __launch_bounds__(kReduceThreads) void sparse_dkv_reduce_kernel(BwdArgs a) {
+  constexpr int ROWS = kReduceThreads * 4 / D;  // key rows per workgroup (4 or 2)
   const int col = blockIdx.x / (kMaskBlock / ROWS);
   const int r0 = (blockIdx.x % (kMaskBlock / ROWS)) * ROWS;
   const int* c4 = a.sp_cols + 4 * (size_t)col;
@@ -721,6 +722,7 @@ __global__ __launch_bounds__(256) void sparse_dkv_reduce_kernel(BwdArgs a) {
   const float* pk = a.dkv_part + (size_t)slot0 * blk + (size_t)row * D + d0;
   const float* pv = pk + (size_t)a.sp_nslots * blk;
   f32x4 sk = *(const f32x4*)pk, sv = *(const f32x4*)pv;
+#pragma unroll 4
   for (int i = 1; i < np; ++i) {
     const f32x4 xk = *(const f32x4*)(pk + i * blk), xv = *(const f32x4*)(pv + i * blk);
     sk[0] += xk[0]; sk[1] += xk[1]; sk[2] += xk[2]; sk[3] += xk[3];
@@ -734,8 +736,8 @@ __global__ __launch_bounds__(256) void sparse_dkv_reduce_kernel(BwdArgs a) {
 // dQ of the block-sparse rows cut into pieces: the pieces' fp32 partials
 // added in piece order and rounded once.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void sparse_dq_reduce_kernel(BwdArgs a) {
-  constexpr int ROWS = 256 * 4 / D;
+__global__ __launch_bounds__(kReduceThreads) void sparse_dq_reduce_kernel(BwdArgs a) {
+  constexpr int ROWS = kReduceThreads * 4 / D;
   const int row = blockIdx.x / (kMaskBlock / ROWS);
   const int r0 = (blockIdx.x % (kMaskBlock / ROWS)) * ROWS;
   const int* c4 = a.sq_rows + 4 * (size_t)row;
@@ -747,6 +749,7 @@ __global__ __launch_bounds__(256) void sparse_dq_reduce_kernel(BwdArgs a) {
   const size_t blk = (size_t)kMaskBlock * D;
   const float* p = a.sq_part + (size_t)slot0 * blk + (size_t)r * D + d0;
   f32x4 acc = *(const f32x4*)p;
+#pragma unroll 4
   for (int i = 1; i < np; ++i) {
     const f32x4 x = *(const f32x4*)(p + i * blk);
     acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
@@ -772,8 +775,8 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (SP && a.sq_items && a.sq_nrows > 0) {
       hipLaunchKernelGGL((sparse_dq_reduce_kernel<T, D>),
-                         dim3((unsigned)((long)a.sq_nrows * (kMaskBlock / (256 * 4 / D)))), dim3(256),
-                         0, st, a);
+                         dim3((unsigned)((long)a.sq_nrows * (kMaskBlock / (kReduceThreads * 4 / D)))),
+                         dim3(kReduceThreads), 0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
@@ -784,8 +787,8 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (SP && a.sp_items && a.sp_ncols > 0) {
       hipLaunchKernelGGL((sparse_dkv_reduce_kernel<T, D>),
-                         dim3((unsigned)((long)a.sp_ncols * (kMaskBlock / (256 * 4 / D)))), dim3(256),
-                         0, st, a);
+                         dim3((unsigned)((long)a.sp_ncols * (kMaskBlock / (kReduceThreads * 4 / D)))),
+                         dim3(kReduceThreads), 0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.gsplit > 1) {

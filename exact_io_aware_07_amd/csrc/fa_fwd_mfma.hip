@@ -385,10 +385,10 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
 // O and LSE of the block-sparse rows cut into pieces: the pieces' (O, LSE)
 // combined by the online-softmax rule, m = max LSE_p, w_p = exp(LSE_p - m),
 // O = sum w_p O_p / sum w_p, LSE = m + ln sum w_p (pieces in order). One
-// workgroup per (row, 256 * 4 / D query rows); thread t covers 4 elements.
+// wave per (row, 256 / D query rows); thread t covers 4 elements.
 template <typename OutT, int D>
-__global__ __launch_bounds__(256) void sparse_o_merge_kernel(FwdArgs a) {
-  constexpr int ROWS = 256 * 4 / D;
+__global__ __launch_bounds__(kReduceThreads) void sparse_o_merge_kernel(FwdArgs a) {
+  constexpr int ROWS = kReduceThreads * 4 / D;
   const int row = blockIdx.x / (kMaskBlock / ROWS);
   const int r0 = (blockIdx.x % (kMaskBlock / ROWS)) * ROWS;
   const int* c4 = a.sp_rows + 4 * (size_t)row;
@@ -405,6 +405,7 @@ __global__ __launch_bounds__(256) void sparse_o_merge_kernel(FwdArgs a) {
   float den = 0.f;
   if (m != -INFINITY) {
     const float* op = a.sp_part + (size_t)slot0 * blk + (size_t)r * D + d0;
+#pragma unroll 4
     for (int i = 0; i < np; ++i) {
       const float w = fast_exp2((lse[i * kMaskBlock] - m) * kLog2e);
       const f32x4 x = *(const f32x4*)(op + i * blk);
@@ -430,9 +431,9 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
                        0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.sp_nrows == 0) return e;
-    const dim3 g((unsigned)((long)a.sp_nrows * (kMaskBlock / (256 * 4 / D))));
-    if (OF) hipLaunchKernelGGL((sparse_o_merge_kernel<float, D>), g, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((sparse_o_merge_kernel<T, D>), g, dim3(256), 0, s, a);
+    const dim3 g((unsigned)((long)a.sp_nrows * (kMaskBlock / (kReduceThreads * 4 / D))));
+    if (OF) hipLaunchKernelGGL((sparse_o_merge_kernel<float, D>), g, dim3(kReduceThreads), 0, s, a);
+    else hipLaunchKernelGGL((sparse_o_merge_kernel<T, D>), g, dim3(kReduceThreads), 0, s, a);
     return hipGetLastError();
   }
   const long nqb = (a.N + kBR - 1) / kBR;

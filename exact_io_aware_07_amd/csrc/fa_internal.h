@@ -97,6 +97,8 @@ struct BwdArgs {
 
 // Blocks per piece of a block-sparse mask row or column.
 constexpr int kSparsePiece = 8;
+// Threads of the kernels that combine the pieces of a cut line: one wave.
+constexpr int kReduceThreads = 64;
 
 // Query-head split of the grouped dK/dV stage for a shape: the smallest
 // divisor of H / Hkv that gives the stage at least two workgroups per

@@ -402,7 +402,9 @@ def _plan_counts(mask, B, H, N, causal, columns):
 def _check_pieces(items, lines, counts):
     """Every line once, whole (first 0, slot -1) when it holds at most 8
     kept blocks, else in pieces of 8 with consecutive slots named by its
-    cut line; the slots of the cut lines tile [0, total); longest first."""
+    cut line; the slots of the cut lines tile [0, total); the items of head
+    bh at positions p with p % 8 == bh % 8 (the XCD of workgroup p) until
+    that class runs out, longest first within each class."""
     seen = {}
     for bh, x, first, slot in items:
         seen.setdefault((bh, x), []).append((first, slot))
@@ -422,8 +424,14 @@ def _check_pieces(items, lines, counts):
     spans = sorted((c[2], c[3]) for c in lines)
     assert [s for s, _ in spans] == [sum(n for _, n in spans[:i]) for i in range(len(spans))]
     size_of = lambda it: min(8, counts[(it[0], it[1])] - it[2])
-    order = [size_of(it) for it in items]
-    assert order == sorted(order, reverse=True) and sorted(order) == sorted(sizes)
+    assert sorted(size_of(it) for it in items) == sorted(sizes)
+    for x in range(8):
+        cls = [size_of(it) for it in items if it[0] % 8 == x]
+        assert cls == sorted(cls, reverse=True)
+        # a position of class x holds another class's item only after class x ran out
+        foreign = [p for p, it in enumerate(items) if p % 8 == x and it[0] % 8 != x]
+        if foreign:
+            assert all(it[0] % 8 != x for it in items[foreign[0]:])
     return sum(n for _, n in spans)
 
 
