@@ -387,22 +387,18 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
         }
       }
     }
-  } else if (my_key < N) {
-    uint16_t* dKg = (uint16_t*)a.dk + head_off + (size_t)my_key * D;
-    uint16_t* dVg = (uint16_t*)a.dv + head_off + (size_t)my_key * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = dt * 32 + r4 * 8 + 4 * hh;
-        const f32x16& K4 = dk[dt];
-        const f32x16& V4 = dv[dt];
-        *(u32x2*)(dKg + d0) = u32x2{Mfma<T>::pack(K4[4 * r4] * a.scale, K4[4 * r4 + 1] * a.scale),
-                                    Mfma<T>::pack(K4[4 * r4 + 2] * a.scale, K4[4 * r4 + 3] * a.scale)};
-        *(u32x2*)(dVg + d0) = u32x2{Mfma<T>::pack(V4[4 * r4], V4[4 * r4 + 1]),
-                                    Mfma<T>::pack(V4[4 * r4 + 2], V4[4 * r4 + 3])};
-      }
-    }
+  } else {
+    // Wave w stages its 32 keys of dK and dV in one of the four query-tile
+    // buffers, free once every wave is past its last tile.
+    constexpr int SB = L::bytes(32);
+    static_assert(2 * SB <= TB, "dK and dV of a wave fit one tile buffer");
+    unsigned char* stage = wave == 0 ? Qs0 : wave == 1 ? Qs1 : wave == 2 ? Gs0 : Gs1;
+    __syncthreads();
+    stage_put<T, D>(stage, dk, a.scale, lane);
+    stage_put<T, D>(stage + SB, dv, 1.f, lane);
+    __syncthreads();
+    stage_rows_out<D>(stage, (uint16_t*)a.dk + head_off + (size_t)key0 * D, N - key0, lane);
+    stage_rows_out<D>(stage + SB, (uint16_t*)a.dv + head_off + (size_t)key0 * D, N - key0, lane);
   }
 }
 
@@ -663,6 +659,9 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
       }
     }
   } else if (my_q < N) {
+    // dQ is written straight from the accumulators: unlike dK, dV, staging
+    // it through LDS measured slower (its lines were not written back more
+    // than once).
     uint16_t* dQg = (uint16_t*)a.dq + head_off + (size_t)my_q * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {

@@ -331,6 +331,52 @@ struct TileLayout {
   static constexpr int rows16() { return (16 / RPI) * GB; }
 };
 
+// An output tile through LDS, so that every store writes whole rows. A lane
+// holds 8 bytes of a row per register group; storing those directly leaves
+// each 128-byte line written in 16-byte parts by 8 separate instructions.
+// Where L2 evicts lines half-written (the dK/dV stage, which streams Q and
+// dO past), those lines are written back more than once.
+//
+// stage_put: a wave's 32 x D accumulator tile (lane l: row l % 32, elements
+// dt * 32 + 8 * r4 + 4 * (l / 32) + [0, 4) in acc[dt][4 * r4 + 0..3]), times
+// mul, rounded to T, into `stage` (TileLayout<D>::bytes(32) bytes).
+//
+// The lane index passes through an empty asm statement so that the offsets
+// derived from it are computed here, after the main loop: hoisted above the
+// loop they would hold registers through it.
+template <typename T, int D>
+__device__ inline void stage_put(unsigned char* stage, const f32x16 (&acc)[D / 32], float mul,
+                                 int lane) {
+  using L = TileLayout<D>;
+  asm volatile("" : "+v"(lane));
+  const int row = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      *(u32x2*)(stage + L::off(row, dt * 4 + r4) + 8 * hh) =
+          u32x2{Mfma<T>::pack(acc[dt][4 * r4] * mul, acc[dt][4 * r4 + 1] * mul),
+                Mfma<T>::pack(acc[dt][4 * r4 + 2] * mul, acc[dt][4 * r4 + 3] * mul)};
+    }
+  }
+}
+
+// stage_rows_out: rows [0, n) (n <= 32; none if n <= 0) of a staged tile to
+// dst, row r at dst + r * D; each store writes 64 / CPR whole rows.
+template <int D>
+__device__ inline void stage_rows_out(const unsigned char* stage, uint16_t* dst, int n, int lane) {
+  using L = TileLayout<D>;
+  constexpr int RPS = 64 / L::CPR;
+  asm volatile("" : "+v"(lane));
+  const int cr = lane / L::CPR, cc = lane % L::CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPS; ++i) {
+    const int row = i * RPS + cr;
+    const u32x4 x = *(const u32x4*)(stage + L::off(row, cc));
+    if (row < n) *(u32x4*)(dst + (size_t)row * D + cc * 8) = x;
+  }
+}
+
 // Each wave of a workgroup of `waves` fills its share of a [rows][D] tile:
 // rows [row0, row0 + rows) of the tensor behind `r` go to `dst` in the
 // TileLayout above. Lane l of the instruction for group G writes position
