@@ -10,10 +10,10 @@
 
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a short
 markdown table. ``counters`` merges ``--pmc`` passes (one CSV each) into one
-table per kernel with ratios that need no normalisation across counter
-instances: share of wave cycles issuing VALU or waiting, LDS bank-conflict
-cycles per LDS-active cycle, L2 hit rate, and VALU / transcendental / LDS
-instructions per MFMA instruction. ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
+table per kernel: MFMA-busy share of SIMD cycles, share of CU cycles with a
+wave resident, share of wave cycles issuing VALU or waiting, LDS
+bank-conflict cycles per LDS-active cycle, L2 hit rate, and VALU /
+transcendental / LDS instructions per MFMA instruction. ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
 WRITE_SIZE, KiB per dispatch) into HBM bytes per launch, each counter scaled
 by what it reads for a plain device copy of known size, and records the hash
 of the kernel sources the counters were taken on, so a stale figure is
@@ -90,8 +90,16 @@ def stats_md(csv_path: str, cmd: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-# derived ratio -> (numerator, denominator)
+# The SQ counters below read for one XCD of the eight: SQ_BUSY_CU_CYCLES /
+# GRBM_GUI_ACTIVE comes to about 30 on full-chip kernels, the CUs of one
+# XCD, not 256. Per-CU and per-SIMD ratios divide by that XCD's units.
+CUS_PER_XCD = 32
+SIMDS_PER_CU = 4
+
+# derived ratio -> (numerator, denominator[, units the denominator counts])
 RATIOS = {
+    "MFMA busy / SIMD cycles": ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", CUS_PER_XCD * SIMDS_PER_CU),
+    "CUs with a wave / CU cycles": ("SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", CUS_PER_XCD),
     "VALU issuing / wave cycles": ("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
     "LDS issuing / wave cycles": ("SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
     "waiting on a counter / wave cycles": ("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
@@ -120,8 +128,9 @@ def counters_md(paths: List[str], workload: str, cmd: str) -> str:
     for short in sorted(per):
         c = per[short]
         cells = []
-        for num, den in RATIOS.values():
-            cells.append(f"{c[num] / c[den]:.3f}" if num in c and c.get(den) else "—")
+        for num, den, *units in RATIOS.values():
+            n_units = units[0] if units else 1
+            cells.append(f"{c[num] / (c[den] * n_units):.3f}" if num in c and c.get(den) else "—")
         hit = c.get("TCC_HIT_sum", c.get("TCC_HIT"))
         miss = c.get("TCC_MISS_sum", c.get("TCC_MISS"))
         cells.append(f"{hit / (hit + miss):.3f}" if hit is not None and miss is not None and hit + miss > 0 else "—")
