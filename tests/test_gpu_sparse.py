@@ -274,3 +274,44 @@ def test_planned_measurement_shapes_sampled_against_oracle(wname):
         e = rel_fro(np64(got), ref)
         print(f"planned full size {wname} {name} rel-fro {e:.2e}", flush=True)
         assert e <= GRAD_REL_FRO, (name, e)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_planned_fp16_per_batch_masks_and_an_empty_batch(causal):
+    """Per-(batch, head) masks with cut rows and columns in both batches, fp16,
+    kv_len = 0 for one batch: the oracle on every output, zeros and -inf
+    where no key is visible."""
+    B, H, N, d = 2, 2, 1300, 64            # 11 blocks, ragged tail
+    kv = [0, 1250]
+    say(f"sparse planned fp16 per-batch masks kv_len={kv} causal={causal}")
+    inp = W.random_case(B, H, N, d, "fp16", seed=77, causal=causal, backward=True, kv_len=kv)
+    mask = W.random_block_mask((B, H), N, 0.5, seed=78)
+    mask[:, 0, :, 1] = 1                  # a long column in head 0 of both batches
+    mask[:, 1, 10, :] = 1                 # a long row (the last block) in head 1
+    o, lse, grads, plan = planned(inp, mask, d ** -0.5, causal, out_dtype=torch.float32)
+    c = plan["counts"].tolist()
+    assert c[2] > 0 and c[5] > 0
+    o_ref, lse_ref = attn_fwd64_sparse(inp["q"], inp["k"], inp["v"], d ** -0.5, causal, kv, mask.numpy())
+    check_fwd(o, lse, o_ref, lse_ref)
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    ref = attn_bwd64_sparse(inp["q"], inp["k"], inp["v"], inp["do"], d ** -0.5, causal, kv, mask.numpy())
+    check_grads(grads, ref, "planned fp16 per-batch")
+    for g in grads:
+        assert torch.all(g[0] == 0)
+
+
+def test_planned_shared_mask_equals_per_head_copies():
+    """One 2-D mask (strides 0) and its per-head copies give the same plan
+    shape and the same bits through the planned entry points."""
+    B, H, N, d = 2, 3, 1500, 128           # 12 blocks
+    say("sparse planned shared vs per-head mask")
+    inp = W.random_case(B, H, N, d, "bf16", seed=80, backward=True)
+    m2 = W.random_block_mask((), N, 0.4, seed=81)
+    m2[:, 0] = 1
+    m2[3, :] = 1
+    a = planned(inp, m2, d ** -0.5, False)
+    b = planned(inp, m2.expand(B, H, *m2.shape).contiguous(), d ** -0.5, False)
+    assert a[3]["counts"].tolist() == b[3]["counts"].tolist()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        assert torch.equal(x, y)
