@@ -420,11 +420,11 @@ struct BlockPick {
 // them resident at once), and later ones go wherever a slot frees. Items
 // stay on the XCD of their index (item 8j + x on XCD x, so a head keeps its
 // K/V in one L2 when nheads is a multiple of 8), and within an XCD the
-// resident set is filled greedily, longest first: round 0 (u < 32) takes the
-// 32 longest items in order, round 1 takes the next 32 in reverse, so the
-// CU with the shortest first item gets the longest second one, and round 2
-// (occ >= 3) gives its longest item to the CU that rounds 0 and 1 left least
-// loaded. Workgroups from round 3 on, and past the resident set, keep
+// resident set is filled greedily, longest first: pass 0 (u < 32) takes the
+// 32 longest items in order, pass 1 takes the next 32 in reverse, so the
+// CU with the shortest first item gets the longest second one, and pass 2
+// (occ >= 3) gives its longest item to the CU that passes 0 and 1 left least
+// loaded. Workgroups from pass 3 on, and past the resident set, keep
 // longest-first order. Any order is correct; this one evens out the work
 // per CU when the whole grid fits on the chip at once (fewer than about
 // three blocks per CU), where plain longest-first order leaves the CUs that
@@ -437,11 +437,11 @@ __device__ inline int causal_item(int bid, int total, int nblk, int nheads, int 
   const int n = (total - x + 7) >> 3;  // workgroups (and items) of this XCD
   const int rho = u / kCusPerXcd;
   const int c = u % kCusPerXcd;
-  const int m = min(n - rho * kCusPerXcd, kCusPerXcd);  // positions used by this round
+  const int m = min(n - rho * kCusPerXcd, kCusPerXcd);  // positions used by this pass
   if (rho == 1) return 8 * (kCusPerXcd + (m - 1 - c)) + x;
-  // Round 2: load of position p after rounds 0 and 1 is w(p) + w(63 - p)
-  // (round 1 is full, since round 2 exists); rank this position among the
-  // round's m positions by that load (ties: lower position first). One lane
+  // Pass 2: load of position p after passes 0 and 1 is w(p) + w(63 - p)
+  // (pass 1 is full, since pass 2 exists); rank this position among the
+  // pass's m positions by that load (ties: lower position first). One lane
   // per position, then a ballot.
   auto w = [&](int j) { return nblk - (8 * j + x) / nheads; };
   const int p = threadIdx.x & (kCusPerXcd - 1);
@@ -482,7 +482,7 @@ __device__ inline int list_mask_blocks(const unsigned char* __restrict__ m, long
     }
     if (on) list[off + __popcll(bal & ((1ull << lane) - 1))] = (unsigned short)blk;
     base += tot;
-    // every wave has read wcount before the next round overwrites it
+    // every wave has read wcount before the next chunk overwrites it
     __syncthreads();
   }
   if (tid < 2) list[base + tid] = base > 0 ? list[base - 1] : (unsigned short)0;
