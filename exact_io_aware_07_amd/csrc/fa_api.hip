@@ -24,8 +24,8 @@ int check_scalars(int B, int H, int N, int d, float scale, int causal) {
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  // The row-sum kernel of the backward packs the fewest rows per block (8),
-  // so it has the largest grid of any launch.
+  // No launch has more than one workgroup per 8 rows (the (O, LSE) merge at
+  // d = 128 has exactly that), so this bounds every grid.
   const long long rows = (long long)B * H * N;
   if (rows / 8 + 1 > kMaxBlocks) return FA_ERR_INVALID_ARG;
   // One head's [N, d] slab is addressed with 32-bit byte offsets (buffer

@@ -38,29 +38,33 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic (fp32). LPR lanes share a row, 16 bytes each.
+// D_i = sum_c dO_ic O_ic (fp32), in the order the dQ kernel forms it (two
+// lanes per row; lane h sums the 8-element chunks 16 c + 8 h, c = 0, 1, ...,
+// in turn; then the two halves are added), so that D, and a backward run as
+// D, dK/dV and dQ stages, equal the one-call backward bit for bit.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dsum_kernel(const uint16_t* __restrict__ o,
                                                    const uint16_t* __restrict__ dout,
                                                    float* __restrict__ dsum, long rows) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
+  constexpr int RPB = 128;  // rows per workgroup
   const int tid = threadIdx.x;
-  const long row = (long)blockIdx.x * RPB + tid / LPR;
-  const int part = tid % LPR;
+  const long row = (long)blockIdx.x * RPB + tid / 2;
+  const int h = tid & 1;
   float acc = 0.f;
   if (row < rows) {
-    const u32x4 ov = *(const u32x4*)(o + row * D + part * 8);
-    const u32x4 gv = *(const u32x4*)(dout + row * D + part * 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(Mfma<T>::to_f32(ov[i] & 0xffffu), Mfma<T>::to_f32(gv[i] & 0xffffu), acc);
-      acc = fmaf(Mfma<T>::to_f32(ov[i] >> 16), Mfma<T>::to_f32(gv[i] >> 16), acc);
+    for (int c = 0; c < D / 16; ++c) {
+      const u32x4 ov = *(const u32x4*)(o + row * D + c * 16 + h * 8);
+      const u32x4 gv = *(const u32x4*)(dout + row * D + c * 16 + h * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(Mfma<T>::to_f32(ov[i] & 0xffffu), Mfma<T>::to_f32(gv[i] & 0xffffu), acc);
+        acc = fmaf(Mfma<T>::to_f32(ov[i] >> 16), Mfma<T>::to_f32(gv[i] >> 16), acc);
+      }
     }
   }
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) dsum[row] = acc;
+  acc += __shfl_xor(acc, 1, 64);
+  if (row < rows && h == 0) dsum[row] = acc;
 }
 
 template <typename T>
@@ -762,7 +766,7 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
   hipError_t e = hipSuccess;
   if (stages & (int)BwdStage::DSUM) {
     const long rows = (long)a.B * a.H * a.N;
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 128;
     hipLaunchKernelGGL((dsum_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                        st, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dsum, rows);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -116,3 +116,39 @@ def test_backward_is_deterministic_and_satisfies_sum_rules():
     assert np.abs(dk.sum(axis=2)).max() <= 2e-2 * np.abs(dk).sum(axis=2).max()
     np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), rtol=0,
                                atol=2e-2 * np.abs(dv).sum(axis=2).max())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_stages_equal_the_one_call_backward(causal, d, dtype):
+    """The exported stages in either order give fa_bwd's results bit for
+    bit: fa_bwd_dq then fa_bwd_dkdv (what fa_bwd enqueues), and fa_bwd_dsum
+    then fa_bwd_dkdv then fa_bwd_dq (the D kernel sums in the dQ kernel's
+    order, so D is the same bits)."""
+    from exact_io_aware_07_amd import fa_bwd, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dsum
+    B, H, N = 2, 3, 333
+    kv = [333, 200]
+    say(f"backward stages vs one call d={d} causal={causal} {dtype}")
+    inp = W.random_case(B, H, N, d, dtype, seed=90 + d, causal=causal, kv_len=kv, backward=True)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    kvt = inp["kv_len"].cuda()
+    sc = d ** -0.5
+    o, lse = run_fwd(inp, sc, causal)
+    ws = torch.empty(B * H * N * 4 + 256, dtype=torch.uint8, device="cuda")
+    g1 = [torch.empty_like(q) for _ in range(3)]
+    fa_bwd(q, k, v, o, do, lse, *g1, sc, causal, kvt, ws)
+    d1 = ws[:B * H * N * 4].view(torch.float32).view(B, H, N).clone()
+    g2 = [torch.empty_like(q) for _ in range(3)]
+    d2 = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa_bwd_dq(q, k, v, o, do, lse, d2, g2[0], sc, causal, kvt)
+    fa_bwd_dkdv(q, k, v, do, lse, d2, g2[1], g2[2], sc, causal, kvt)
+    g3 = [torch.empty_like(q) for _ in range(3)]
+    d3 = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa_bwd_dsum(o, do, d3)
+    fa_bwd_dkdv(q, k, v, do, lse, d3, g3[1], g3[2], sc, causal, kvt)
+    fa_bwd_dq(q, k, v, o, do, lse, d3, g3[0], sc, causal, kvt)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(d1, d3)
+    for a, b, c in zip(g1, g2, g3):
+        assert torch.equal(a, b) and torch.equal(a, c)
