@@ -170,7 +170,8 @@ def attn_fwd64_fp8(qz: dict, scale: float, causal: bool = False, kv_len=None, ti
                 s = np.where(vis, s, -np.inf)
                 m_new = np.maximum(m, s.max(axis=1))
                 grow = m_new > m
-                alpha = np.where(grow, np.exp(np.where(grow, m - m_new, 0.0)), 1.0)
+                # m - m_new only where the max grew (elsewhere both may be -inf)
+                alpha = np.where(grow, np.exp(np.subtract(m, m_new, out=np.zeros_like(m), where=grow)), 1.0)
                 l *= alpha
                 acc *= alpha[:, None]
                 m_safe = np.where(np.isfinite(m_new), m_new, 0.0)
