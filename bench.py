@@ -610,7 +610,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               "the per-head work is independent and would shard by (batch, head) with no "
               "exchange, but only the single-GPU path exists", file=sys.stderr)
         raise SystemExit(2)
