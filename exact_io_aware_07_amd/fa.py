@@ -616,3 +616,36 @@ def attention_backward(q, k, v, o, dout, lse, causal: bool = False, kv_len=None,
     else:
         fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len, None, stream)
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """Autograd glue: the forward keeps O and LSE, the backward recomputes
+    from them through the library (no N x N tensor is ever formed)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal: bool, scale: float, kv_len):
+        o, lse = attention_forward(q, k, v, causal=causal, kv_len=kv_len, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.kv_len, ctx.causal, ctx.scale = kv_len, causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = attention_backward(q, k, v, o, dout.contiguous(), lse, causal=ctx.causal,
+                                        kv_len=ctx.kv_len, scale=ctx.scale)
+        return dq, dk, dv, None, None, None
+
+
+def scaled_dot_product_attention(q, k, v, is_causal: bool = False, scale: Optional[float] = None,
+                                 kv_len=None) -> torch.Tensor:
+    """softmax(scale * Q K^T) V with autograd, in the shape convention of
+    torch's scaled_dot_product_attention (q [B, H, N, d]; k, v [B, H or H_kv,
+    N, d]; top-left causal mask; scale defaults to 1 / sqrt(d)), plus per-batch
+    key lengths kv_len (int32 [B] on the device, or None). Inputs must be
+    contiguous fp16 / bf16 / fp32 device tensors of head dim 64 or 128; no
+    dropout and no arbitrary mask. Forward and backward run the library's
+    kernels (fa_fwd / fa_bwd, or the grouped-query entry points)."""
+    d = q.shape[-1]
+    return _Attention.apply(q, k, v, bool(is_causal), d ** -0.5 if scale is None else float(scale),
+                            kv_len)

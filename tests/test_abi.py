@@ -519,3 +519,10 @@ def test_sparse_planned_validation():
                                    fa.FA_BF16) == fa.FA_OK
     assert L.fa_bwd_sparse_planned(*([None] * 9), 1, 2, 0, 64, 0.125, 0, None, None, 0, 0, None,
                                    C(0, 0, 0, 0, 0, 0, 0, 0), None, 0, None, fa.FA_BF16) == fa.FA_OK
+
+
+def test_autograd_wrapper_refuses_host_tensors_instead_of_computing():
+    from exact_io_aware_07_amd import scaled_dot_product_attention
+    q = torch.randn(1, 1, 16, 64, dtype=torch.bfloat16, requires_grad=True)
+    with pytest.raises(ValueError, match="device tensor"):
+        scaled_dot_product_attention(q, q, q)

@@ -1,0 +1,58 @@
+"""The autograd wrapper scaled_dot_product_attention: its output and the
+gradients torch's autograd computes through it are the library's own
+(fa_fwd / fa_bwd bit for bit, grouped-query heads included) and match the
+fp64 oracle to the usual bounds."""
+import pytest
+import torch
+
+from exact_io_aware_07_amd import (attention_backward, attention_forward,
+                                   scaled_dot_product_attention)
+from exact_io_aware_07_amd import workloads as W
+from helpers import (F32_GRAD_REL_FRO, F32_MAX_ABS, FWD_MAX_ABS, GRAD_REL_FRO, np64, rel_fro,
+                     say)
+from oracle import attn_bwd64, attn_fwd64
+from oracle.gqa import attn_bwd64_gqa, attn_fwd64_gqa
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # (B, H, Hkv, N, d, dtype, causal, kv_len)
+    (2, 2, 2, 300, 64, "bf16", True, None),
+    (1, 3, 3, 129, 128, "fp16", False, [100]),
+    (2, 4, 2, 257, 64, "bf16", True, [257, 40]),
+    (1, 2, 2, 200, 64, "fp32", True, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c[:6])) + f"-c{int(c[6])}")
+def test_autograd_equals_the_library_and_the_oracle(case):
+    B, H, Hkv, N, d, dtype, causal, kv = case
+    say(f"autograd {case}")
+    inp = W.random_case(B, H, N, d, dtype, seed=N + d, causal=causal, kv_len=kv, backward=True,
+                        Hkv=Hkv if Hkv != H else None)
+    q, k, v, do = (inp[n].cuda().requires_grad_(n != "do") for n in ("q", "k", "v", "do"))
+    kvt = None if kv is None else inp["kv_len"].cuda()
+    sc = d ** -0.5
+    o = scaled_dot_product_attention(q, k, v, is_causal=causal, kv_len=kvt)
+    (o * do).sum().backward()
+    torch.cuda.synchronize()
+    # the same bits as the plain calls
+    o2, lse2 = attention_forward(q.detach(), k.detach(), v.detach(), causal, kvt, sc)
+    g2 = attention_backward(q.detach(), k.detach(), v.detach(), o2, do, lse2, causal, kvt, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o2)
+    for t, g in zip((q, k, v), g2):
+        assert torch.equal(t.grad, g)
+    # and the oracle
+    if Hkv != H:
+        o_ref, _ = attn_fwd64_gqa(inp["q"], inp["k"], inp["v"], sc, causal, kv)
+        ref = attn_bwd64_gqa(inp["q"], inp["k"], inp["v"], inp["do"], sc, causal, kv)
+    else:
+        o_ref, _ = attn_fwd64(inp["q"], inp["k"], inp["v"], sc, causal, kv)
+        ref = attn_bwd64(inp["q"], inp["k"], inp["v"], inp["do"], sc, causal, kv)
+    f32 = dtype == "fp32"
+    err = float(abs(np64(o.detach().float()) - o_ref).max())
+    # storage-dtype O: its own rounding plus the forward bound
+    assert err <= (F32_MAX_ABS if f32 else FWD_MAX_ABS + 1e-2), err
+    for t, r in zip((q, k, v), ref):
+        e = rel_fro(np64(t.grad), r)
+        assert e <= (F32_GRAD_REL_FRO if f32 else GRAD_REL_FRO), e
