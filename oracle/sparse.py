@@ -106,7 +106,8 @@ def attn_bwd64_sparse_sampled(q, k, v, dout, scale: float, causal: bool, kv_len,
     """The gradients of ``attn_bwd64_sparse`` on sampled query rows (dQ) and
     keys (dK, dV) of the listed (b, h) heads, for N too long for an N x N
     matrix. Per head, LSE_i and D_i = sum_j P_ij dP_ij come from whole rows
-    taken ``row_chunk`` at a time; then
+    taken ``row_chunk`` at a time (only the rows that a sampled row or key
+    needs); then
       dQ_i = scale sum_j P_ij (dP_ij - D_i) K_j   (whole rows i in q_rows)
       dK_j = scale sum_i P_ij (dP_ij - D_i) Q_i   (whole columns j in k_rows)
       dV_j = sum_i P_ij dO_i
@@ -123,10 +124,19 @@ def attn_bwd64_sparse_sampled(q, k, v, dout, scale: float, causal: bool, kv_len,
     for t, (b, h) in enumerate(heads):
         m = _mask_of(block_mask, b, h)
         lim = int(lens[b])
-        lse = np.empty(N)
-        dsum = np.empty(N)
-        for c0 in range(0, N, row_chunk):
-            part = np.arange(c0, min(c0 + row_chunk, N))
+        # LSE_i and D_i are needed for the sampled rows and for every row whose
+        # mask row keeps the block of a sampled key; the other rows see none
+        # of those keys, so they stay at -inf / 0 and give P = 0 below.
+        need = np.zeros(N, dtype=bool)
+        need[qr] = True
+        if len(kr):
+            kept = (np.asarray(m) != 0)[:, np.unique(kr // block)].any(axis=1)
+            need |= np.repeat(kept, block)[:N]
+        lse = np.full(N, -np.inf)
+        dsum = np.zeros(N)
+        rows_needed = np.nonzero(need)[0]
+        for c0 in range(0, len(rows_needed), row_chunk):
+            part = rows_needed[c0:c0 + row_chunk]
             vis = sparse_visible(N, causal, lim, m, block, rows=part)
             p, lse[part] = _probs(q[b, h, part], k[b, h], vis, scale)
             dsum[part] = (p * (dout[b, h, part] @ v[b, h].T)).sum(axis=1)

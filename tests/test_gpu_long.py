@@ -55,3 +55,49 @@ def test_backward_at_262144_tokens():
     dv_abs = np.abs(np64(dv[0, 0])).sum(axis=0)
     gap = np.abs(dv_sum - np64(inp["do"][0, 0]).sum(axis=0))
     assert np.all(gap <= 2 ** -8 * (do_abs + dv_abs)), gap.max()
+
+
+def test_planned_sparse_at_the_largest_mask():
+    """Block-sparse attention at 4096 mask blocks (N = 524,288), the most a
+    mask row or column may hold: a band of three plus a global first block,
+    so row 0 and column 0 keep all 4096 blocks (512 pieces each in the
+    plan). O, LSE and dQ of sampled rows and dK, dV of keys that few rows
+    see against the oracle; all of dV against sum_j dV_j = sum_i dO_i."""
+    from exact_io_aware_07_amd import fa_bwd_sparse_planned, fa_fwd_sparse_planned, fa_sparse_plan
+    from oracle import attn_bwd64_sparse_sampled, attn_fwd64_sparse
+    N, d = 4096 * 128, 64
+    w = W.SPARSE_GLOBAL.with_(H=1, N=N)
+    say(f"planned sparse at the largest mask N={N}")
+    inp = W.random_case(1, 1, N, d, "bf16", seed=52, backward=True)
+    mask = W.block_mask(w)
+    plan = fa_sparse_plan(mask, 1, 1, N, False)
+    assert plan["counts"][2] == 512 and plan["counts"][5] == 512
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    m = mask.cuda()
+    o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    fa_fwd_sparse_planned(q, k, v, o, lse, m, plan, d ** -0.5, False)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    fa_bwd_sparse_planned(q, k, v, o.to(q.dtype), do, lse, *grads, m, plan, d ** -0.5, False)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 300000, N - 129, N - 1]
+    o_ref, lse_ref = attn_fwd64_sparse(inp["q"], inp["k"], inp["v"], d ** -0.5, False, None,
+                                       mask.numpy(), rows=rows, row_chunk=2)
+    st = fwd_stats(np64(o[:, :, rows]), np64(lse[:, :, rows]), o_ref, lse_ref)
+    print(f"N={N} {st}", flush=True)
+    assert st["max_abs"] <= FWD_MAX_ABS and st["lse_max_abs"] <= LSE_MAX_ABS, st
+    keys = [N - 1, N - 100, 300000, 300001]
+    sq, sk, sv = attn_bwd64_sparse_sampled(inp["q"], inp["k"], inp["v"], inp["do"], d ** -0.5,
+                                           False, None, mask.numpy(), [(0, 0)], rows[1:], keys,
+                                           row_chunk=64)
+    dq, dk, dv = grads
+    errs = {"dq": rel_fro(np64(dq[0, 0, rows[1:]]), sq[0]), "dk": rel_fro(np64(dk[0, 0, keys]), sk[0]),
+            "dv": rel_fro(np64(dv[0, 0, keys]), sv[0])}
+    print(f"N={N} rel-fro {errs}", flush=True)
+    for n, e in errs.items():
+        assert e <= GRAD_REL_FRO, (n, e)
+    dv_sum = np64(dv[0, 0]).sum(axis=0)
+    do_abs = np.abs(np64(inp["do"][0, 0])).sum(axis=0)
+    dv_abs = np.abs(np64(dv[0, 0])).sum(axis=0)
+    gap = np.abs(dv_sum - np64(inp["do"][0, 0]).sum(axis=0))
+    assert np.all(gap <= 2 ** -8 * (do_abs + dv_abs)), gap.max()

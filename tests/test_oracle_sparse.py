@@ -161,3 +161,13 @@ def test_sampled_rows_and_keys_match_the_whole_backward(causal):
         np.testing.assert_allclose(sq[t], dq[b, h, rows], atol=1e-12)
         np.testing.assert_allclose(sk[t], dk[b, h, rows], atol=1e-12)
         np.testing.assert_allclose(sv[t], dv[b, h, rows], atol=1e-12)
+    # rows alone and keys alone (each then forms LSE and D only where needed)
+    keys = [1, 5, 30]
+    sq2, _, _ = attn_bwd64_sparse_sampled(q, k, v, do, 0.6, causal, kv, mask, heads, rows, [],
+                                          block=blk, row_chunk=3)
+    _, sk2, sv2 = attn_bwd64_sparse_sampled(q, k, v, do, 0.6, causal, kv, mask, heads, [], keys,
+                                            block=blk, row_chunk=3)
+    for t, (b, h) in enumerate(heads):
+        np.testing.assert_allclose(sq2[t], dq[b, h, rows], atol=1e-12)
+        np.testing.assert_allclose(sk2[t], dk[b, h, keys], atol=1e-12)
+        np.testing.assert_allclose(sv2[t], dv[b, h, keys], atol=1e-12)
