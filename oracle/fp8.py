@@ -141,26 +141,29 @@ def fp8_quantize(q, k, v, signs=None, block_q: int = 128, block_k: int = 64):
 
 def attn_fwd64_fp8(qz: dict, scale: float, causal: bool = False, kv_len=None, tile: int = 64,
                    block_q: int = 128, block_k: int = 64, p_scale: float = 256.0,
-                   quantize_p: bool = True):
+                   quantize_p: bool = True, rows=None):
     """Attention over the quantised inputs of ``fp8_quantize`` (tile by tile,
     P quantised per tile; see the module text). ``quantize_p=False`` skips
-    the quantisation of P (for pinning the rest). Returns (O [B, H, N, d],
-    LSE [B, H, N]) in fp64."""
+    the quantisation of P (for pinning the rest); ``rows`` restricts the
+    output to those query rows (each still against all its keys). Returns
+    (O [B, H, R, d], LSE [B, H, R]) in fp64."""
     q8, k8, v8 = qz["q8"], qz["k8"], qz["v8"]
     B, H, N, d = q8.shape
     lens = _kv_lens(kv_len, B, N)
-    rows = np.arange(N)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = len(rows)
     s_mul = scale / (d if qz["rotated"] else 1)
-    o = np.zeros((B, H, N, d))
-    lse = np.zeros((B, H, N))
+    o = np.zeros((B, H, R, d))
+    lse = np.zeros((B, H, R))
     for b in range(B):
         for h in range(H):
-            qd = e4m3_decode(q8[b, h]) * np.repeat(qz["sq"][b, h].astype(np.float64), block_q)[:N, None]
+            qd = (e4m3_decode(q8[b, h][rows]) *
+                  qz["sq"][b, h].astype(np.float64)[rows // block_q][:, None])
             kd = e4m3_decode(k8[b, h]) * np.repeat(qz["sk"][b, h].astype(np.float64), block_k)[:N, None]
             vd = e4m3_decode(v8[b, h])
-            m = np.full(N, -np.inf)
-            l = np.zeros(N)
-            acc = np.zeros((N, d))
+            m = np.full(R, -np.inf)
+            l = np.zeros(R)
+            acc = np.zeros((R, d))
             for t0 in range(0, N, tile):
                 cols = np.arange(t0, min(t0 + tile, N))
                 s = s_mul * (qd @ kd[cols].T)

@@ -169,3 +169,29 @@ def test_end_to_end_error_and_the_rotation_on_outlier_channels():
     # least halves the error.
     assert errs["rotated"] < 0.15
     assert errs["rotated"] < 0.5 * errs["plain"]
+
+
+def test_long_sequence_codes_and_sampled_rows():
+    """N = 131,072 at d = 128 (1,024 query blocks, 2,048 key scales, a V^T
+    row of 131,072 codes): codes and scales bit for bit, and O, LSE of
+    sampled rows against the oracle's FP8 attention on the same codes."""
+    B, H, N, d = 1, 1, 1 << 17, 128
+    say(f"fp8 long N={N}")
+    inp = W.random_case(B, H, N, d, "bf16", seed=71)
+    signs = W.random_signs(d, seed=72)
+    bufs = gpu_quantize(inp, signs)
+    ref = fp8_quantize(inp["q"], inp["k"], inp["v"], signs.numpy())
+    np.testing.assert_array_equal(bufs["q8"].cpu().numpy(), ref["q8"])
+    np.testing.assert_array_equal(bufs["k8"].cpu().numpy(), ref["k8"])
+    np.testing.assert_array_equal(np.swapaxes(bufs["vt8"].cpu().numpy()[..., :N], -1, -2), ref["v8"])
+    for name, key in (("q_scale", "sq"), ("k_scale", "sk"), ("v_scale", "sv")):
+        np.testing.assert_array_equal(bufs[name].cpu().numpy(), ref[key])
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa_fwd_fp8(bufs, True, o, lse, d ** -0.5, True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 65535, 65536, N - 65, N - 1]
+    o_ref, lse_ref = attn_fwd64_fp8(ref, d ** -0.5, True, rows=rows)
+    st = fwd_stats(np64(o[:, :, rows]), np64(lse[:, :, rows]), o_ref, lse_ref)
+    print(f"N={N} {st}", flush=True)
+    assert st["max_abs"] <= O_MAX and st["mean_abs"] <= O_MEAN and st["lse_max_abs"] <= LSE_MAX, st

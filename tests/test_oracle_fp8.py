@@ -227,3 +227,19 @@ def test_p_is_quantised_against_the_running_max():
     expect = (a * vd[:64].sum(axis=0) + vd[64]) / (64 * a + 1)
     np.testing.assert_allclose(o[0, 0, 0], expect, atol=1e-12)
     assert abs(lse[0, 0, 0] - (c + math.log(64 * a + 1))) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_subset_equals_the_whole(causal):
+    """``rows`` only selects outputs: each selected row is the same as in the
+    whole computation (the row's own query block scale, all its keys)."""
+    rng = np.random.default_rng(11)
+    B, H, N, d = 2, 1, 300, 64
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    qz = fp8_quantize(q, k, v, np.where(rng.random(d) < 0.5, -1, 1))
+    o, lse = attn_fwd64_fp8(qz, 0.125, causal, [300, 170])
+    rows = [0, 5, 127, 128, 169, 170, 299]
+    o_r, lse_r = attn_fwd64_fp8(qz, 0.125, causal, [300, 170], rows=rows)
+    # equal up to fp64 rounding (the products are blocked differently)
+    np.testing.assert_allclose(o_r, o[:, :, rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse_r, lse[:, :, rows], rtol=0, atol=1e-12)
