@@ -6,7 +6,10 @@ is large and the grid is long, checked where the fp64 oracle can follow.
   * backward at 262,144 tokens (causal, one head): dQ of sampled rows and
     dK, dV of the last keys (which only the last rows see) against the
     oracle, and for all of dV the identity that holds at any size:
-    sum_j dV_j = sum_i dO_i (each row's probabilities sum to one).
+    sum_j dV_j = sum_i dO_i (each row's probabilities sum to one);
+  * planned block-sparse attention at the largest mask (4096 blocks);
+  * multi-query attention at 65,536 tokens, where the grouped dK/dV stage
+    adds the fp32 partials of two shares.
 """
 import numpy as np
 import pytest
@@ -101,3 +104,34 @@ def test_planned_sparse_at_the_largest_mask():
     dv_abs = np.abs(np64(dv[0, 0])).sum(axis=0)
     gap = np.abs(dv_sum - np64(inp["do"][0, 0]).sum(axis=0))
     assert np.all(gap <= 2 ** -8 * (do_abs + dv_abs)), gap.max()
+
+
+def test_multi_query_backward_at_65536_tokens():
+    """Multi-query attention (4 query heads on one K/V head) at N = 65,536,
+    causal, d = 64: the grid is small enough that the grouped dK/dV stage
+    cuts the group into two shares and adds their fp32 partials. dQ of
+    sampled rows of every query head, and dK, dV (summed over the group) of
+    the last keys, against the oracle on K/V repeated over the group."""
+    from exact_io_aware_07_amd import attention_backward, attention_forward
+    N, d, H = 1 << 16, 64, 4
+    say(f"long multi-query backward N={N}")
+    inp = W.random_case(1, H, N, d, "bf16", seed=53, causal=True, backward=True, Hkv=1)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    sc = d ** -0.5
+    o, lse = attention_forward(q, k, v, True, None, sc)
+    dq, dk, dv = attention_backward(q, k, v, o, do, lse, True, None, sc)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 40000, N - 1]
+    keys = [N - 1, N - 2, N - 64, N - 65, N - 130]
+    kg, vg = inp["k"].repeat_interleave(H, dim=1), inp["v"].repeat_interleave(H, dim=1)
+    heads = [(0, h) for h in range(H)]
+    sq, _, _ = attn_bwd64_sampled(inp["q"], kg, vg, inp["do"], sc, True, heads=heads, q_rows=rows,
+                                  k_rows=[], row_chunk=4)
+    _, sk, sv = attn_bwd64_sampled(inp["q"], kg, vg, inp["do"], sc, True, heads=heads, q_rows=[],
+                                   k_rows=keys, row_chunk=64)
+    errs = {"dq": rel_fro(np64(dq[0][:, rows]), np.asarray(sq)),
+            "dk": rel_fro(np64(dk[0, 0, keys]), np.asarray(sk).sum(axis=0)),
+            "dv": rel_fro(np64(dv[0, 0, keys]), np.asarray(sv).sum(axis=0))}
+    print(f"N={N} rel-fro {errs}", flush=True)
+    for n, e in errs.items():
+        assert e <= GRAD_REL_FRO, (n, e)
