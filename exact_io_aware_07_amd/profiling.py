@@ -11,7 +11,9 @@
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a short
 markdown table. ``counters`` merges ``--pmc`` passes (one CSV each) into one
 table per kernel: MFMA-busy share of SIMD cycles, share of CU cycles with a
-wave resident, share of wave cycles issuing VALU or waiting, LDS
+wave resident, share of SIMD cycles with MFMA and VALU both executing, share
+of wave cycles issuing VALU, waiting (s_waitcnt, barriers) or waiting to
+issue (dependencies, arbitration), LDS
 bank-conflict cycles per LDS-active cycle, L2 hit rate, and VALU /
 transcendental / LDS instructions per MFMA instruction. ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
 WRITE_SIZE, KiB per dispatch) into HBM bytes per launch, each counter scaled
@@ -100,9 +102,12 @@ SIMDS_PER_CU = 4
 RATIOS = {
     "MFMA busy / SIMD cycles": ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", CUS_PER_XCD * SIMDS_PER_CU),
     "CUs with a wave / CU cycles": ("SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", CUS_PER_XCD),
+    "MFMA and VALU together / SIMD cycles": ("SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE",
+                                             CUS_PER_XCD * SIMDS_PER_CU),
     "VALU issuing / wave cycles": ("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+    "waiting (s_waitcnt, barrier) / wave cycles": ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
     "LDS issuing / wave cycles": ("SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
-    "waiting on a counter / wave cycles": ("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    "waiting to issue / wave cycles": ("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
     "LDS bank-conflict / LDS-active cycles": ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
     "VALU insts / MFMA inst": ("SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
     "transcendental insts / MFMA inst": ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA"),
