@@ -109,7 +109,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *   fa_bwd_dkdv: reads q, k, v, dout, lse, dsum; writes dk, dv. dsum must
  *                hold D_i, from fa_bwd_dq or fa_bwd_dsum, before it runs.
  *   fa_bwd_dsum: reads o, dout; writes dsum. The same D_i on its own, for a
- *                caller that wants dK/dV without dQ.
+ *                caller that wants dK/dV without dQ. It sums in the order
+ *                fa_bwd_dq does, so either order of stages gives fa_bwd's
+ *                dsum, dq, dk and dv bit for bit.
  * Errors as for fa_bwd (no FA_ERR_WORKSPACE: dsum is a plain argument).
  */
 int fa_bwd_dsum(const void* o, const void* dout, float* dsum, int B, int H,
