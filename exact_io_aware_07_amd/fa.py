@@ -453,7 +453,9 @@ def fa_bwd_sparse_planned_workspace_bytes(B: int, H: int, N: int, d: int, counts
 
 
 def _plan_args(plan: dict, device):
-    """(device plan, CPU counts) of a plan from fa_sparse_plan."""
+    """(device plan, CPU counts) of a plan from fa_sparse_plan. A plan whose
+    "plan" tensor is already on the device is used in place; a host one is
+    copied on every call (a copy that graph capture cannot record)."""
     counts = torch.as_tensor(plan["counts"], dtype=torch.int32).contiguous()
     if counts.is_cuda or counts.numel() != 8:
         raise ValueError("plan['counts'] must be the 8 host counts of fa_sparse_plan")
