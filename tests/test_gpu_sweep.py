@@ -48,7 +48,7 @@ def draw(i: int) -> dict:
             "long_col": r.random(), "long_row": r.random()}
 
 
-CASES = [draw(i) for i in range(45)]
+CASES = [draw(i) for i in range(300)]
 
 
 def _id(c):
