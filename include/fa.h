@@ -37,7 +37,11 @@
  *  - A query row with no visible key gets O = 0 and LSE = -inf (no NaN).
  *  - stream: a hipStream_t passed as void* (NULL = the null stream). Work is
  *    enqueued asynchronously; FA_OK means "enqueued". A device fault shows
- *    at the caller's next synchronisation.
+ *    at the caller's next synchronisation. On the device side a call only
+ *    launches kernels on that stream (no allocation, copy, memset or
+ *    synchronisation), so it may be recorded under HIP stream capture. The
+ *    only host memory a call reads is read during the call itself (the
+ *    counts of the planned block-sparse calls, the mask of fa_sparse_plan).
  *  - Argument validation happens on the host before any HIP call, so every
  *    FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED / FA_ERR_WORKSPACE return has
  *    launched nothing.
