@@ -92,9 +92,11 @@ def stats_md(csv_path: str, cmd: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-# The SQ counters below read for one XCD of the eight: SQ_BUSY_CU_CYCLES /
-# GRBM_GUI_ACTIVE comes to about 30 on full-chip kernels, the CUs of one
-# XCD, not 256. Per-CU and per-SIMD ratios divide by that XCD's units.
+# Every XCD has its own GRBM and SQs, and rocprofv3 sums each counter over
+# the eight: GRBM_GUI_ACTIVE reads eight times the kernel's cycles, and
+# SQ_BUSY_CU_CYCLES / GRBM_GUI_ACTIVE comes to about 30 on full-chip kernels
+# (32 CUs per GRBM). So per-CU and per-SIMD ratios divide the GRBM count by
+# the units of one XCD.
 CUS_PER_XCD = 32
 SIMDS_PER_CU = 4
 
