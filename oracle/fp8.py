@@ -141,12 +141,24 @@ def fp8_quantize(q, k, v, signs=None, block_q: int = 128, block_k: int = 64):
 
 def attn_fwd64_fp8(qz: dict, scale: float, causal: bool = False, kv_len=None, tile: int = 64,
                    block_q: int = 128, block_k: int = 64, p_scale: float = 256.0,
-                   quantize_p: bool = True, rows=None):
+                   quantize_p: bool = True, rows=None, s_err: float = 0.0):
     """Attention over the quantised inputs of ``fp8_quantize`` (tile by tile,
     P quantised per tile; see the module text). ``quantize_p=False`` skips
     the quantisation of P (for pinning the rest); ``rows`` restricts the
     output to those query rows (each still against all its keys). Returns
-    (O [B, H, R, d], LSE [B, H, R]) in fp64."""
+    (O [B, H, R, d], LSE [B, H, R]) in fp64.
+
+    ``s_err > 0`` also returns, per row, how far O can move when the P codes
+    are decided by an implementation whose scores each carry an error of up
+    to s_err times the sum of their products' magnitudes (fp32 accumulation
+    on the matrix cores). The exponent of p_j = exp(s_j - m) is then off by
+    at most e_j = scale' (A_j + max A), A_j = sum_c |q_c k_jc| (its own score
+    and the row max), so a code is open to either neighbour when rounding
+    p exp(-e_j) and p exp(e_j) gives different codes. Returned is the largest
+    change one such key can make: the gap between those two codes times the
+    key's largest |V| entry, weighted and normalised as O is. Every other
+    code is unique. (A quantised value decided by floating point admits more
+    than one correct result near a rounding boundary.)"""
     q8, k8, v8 = qz["q8"], qz["k8"], qz["v8"]
     B, H, N, d = q8.shape
     lens = _kv_lens(kv_len, B, N)
@@ -155,6 +167,7 @@ def attn_fwd64_fp8(qz: dict, scale: float, causal: bool = False, kv_len=None, ti
     s_mul = scale / (d if qz["rotated"] else 1)
     o = np.zeros((B, H, R, d))
     lse = np.zeros((B, H, R))
+    flip_out = np.zeros((B, H, R))
     for b in range(B):
         for h in range(H):
             qd = (e4m3_decode(q8[b, h][rows]) *
@@ -164,6 +177,17 @@ def attn_fwd64_fp8(qz: dict, scale: float, causal: bool = False, kv_len=None, ti
             m = np.full(R, -np.inf)
             l = np.zeros(R)
             acc = np.zeros((R, d))
+            flip = np.zeros(R)
+            vmax = np.abs(vd).max(axis=1) if N else np.zeros(0)
+            amag_max = np.zeros(R)
+            if quantize_p and s_err > 0 and N:
+                # largest score magnitude sum over the row's visible keys
+                am = s_mul * (np.abs(qd) @ np.abs(kd).T)
+                keys = np.arange(N)[None, :]
+                vis_all = keys < lens[b]
+                if causal:
+                    vis_all = vis_all & (keys <= rows[:, None])
+                amag_max = np.where(vis_all, am, 0.0).max(axis=1)
             for t0 in range(0, N, tile):
                 cols = np.arange(t0, min(t0 + tile, N))
                 s = s_mul * (qd @ kd[cols].T)
@@ -177,13 +201,24 @@ def attn_fwd64_fp8(qz: dict, scale: float, causal: bool = False, kv_len=None, ti
                 alpha = np.where(grow, np.exp(np.subtract(m, m_new, out=np.zeros_like(m), where=grow)), 1.0)
                 l *= alpha
                 acc *= alpha[:, None]
+                flip *= alpha
                 m_safe = np.where(np.isfinite(m_new), m_new, 0.0)
                 p = np.where(vis, np.exp(s - m_safe[:, None]), 0.0)
                 l += p.sum(axis=1)
                 pq = e4m3_decode(e4m3_encode(p * p_scale)) / p_scale if quantize_p else p
                 acc += pq @ vd[cols]
+                if quantize_p and s_err > 0:
+                    amag = s_mul * (np.abs(qd) @ np.abs(kd[cols]).T)
+                    e = s_err * (amag + amag_max[:, None])
+                    x = p * p_scale
+                    gap = (e4m3_decode(e4m3_encode(x * np.exp(e))) -
+                           e4m3_decode(e4m3_encode(x * np.exp(-e)))) / p_scale
+                    flip = np.maximum(flip, (np.abs(gap) * vmax[cols][None, :]).max(axis=1))
                 m = m_new
             has = l > 0
             o[b, h] = np.where(has[:, None], acc * float(qz["sv"][b, h]) / np.where(has, l, 1.0)[:, None], 0.0)
             lse[b, h] = np.where(has, m + np.log(np.where(has, l, 1.0)), -np.inf)
+            flip_out[b, h] = np.where(has, flip * float(qz["sv"][b, h]) / np.where(has, l, 1.0), 0.0)
+    if s_err > 0:
+        return o, lse, flip_out
     return o, lse

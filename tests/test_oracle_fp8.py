@@ -243,3 +243,70 @@ def test_row_subset_equals_the_whole(causal):
     # equal up to fp64 rounding (the products are blocked differently)
     np.testing.assert_allclose(o_r, o[:, :, rows], rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse_r, lse[:, :, rows], rtol=0, atol=1e-12)
+
+
+def test_flip_bound_leaves_o_and_lse_unchanged():
+    rng = np.random.default_rng(31)
+    q, k, v = (rng.standard_normal((1, 2, 200, 64)) for _ in range(3))
+    qz = fp8_quantize(q, k, v, np.where(rng.random(64) < 0.5, -1, 1))
+    o, lse = attn_fwd64_fp8(qz, 0.125, True, None)
+    o2, lse2, flip = attn_fwd64_fp8(qz, 0.125, True, None, s_err=2e-4)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    assert flip.shape == lse.shape and np.all(flip >= 0) and flip.max() > 0
+    _, _, none = attn_fwd64_fp8(qz, 0.125, True, None, s_err=1e-14)
+    assert np.all(none == 0)
+
+
+def test_flip_bound_of_one_open_code_closed_form():
+    # scores 0 and c = -0.625 (on the e4m3 grid): 256 e^c = 137.03 lies 0.76%
+    # above the rounding boundary 136 between the codes 128 and 144. The
+    # exponent error bound is s_err (|c| + |c|): open for s_err = 0.01, closed
+    # for s_err = 0.001.
+    c = -0.625
+    q, k, v = one_row_case([0.0, c], 22)
+    qz = fp8_quantize(q, k, v, None)
+    p1 = math.exp(c)
+    assert py_decode(py_encode(256 * p1)) == 144
+    vd = e4m3_decode(qz["v8"][0, 0]).astype(np.float64)
+    _, _, f_open = attn_fwd64_fp8(qz, 1.0, False, None, s_err=0.01)
+    expect = (16 / 256) * np.abs(vd[1]).max() * float(qz["sv"][0, 0]) / (1 + p1)
+    assert abs(f_open[0, 0, 0] - expect) < 1e-13
+    _, _, f_closed = attn_fwd64_fp8(qz, 1.0, False, None, s_err=0.001)
+    assert f_closed[0, 0, 0] == 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_flip_bound_covers_every_single_code_move(causal):
+    """Brute force over one tile: moving any one open code of a row to its
+    other candidate changes that row of O by no more than the bound."""
+    rng = np.random.default_rng(40 + causal)
+    N, d, scale, s_err = 40, 64, 0.125, 2e-3
+    q, k, v = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    qz = fp8_quantize(q, k, v, None)
+    o, _, flip = attn_fwd64_fp8(qz, scale, causal, None, s_err=s_err)
+    qd = e4m3_decode(qz["q8"][0, 0]) * float(qz["sq"][0, 0, 0])
+    kd = e4m3_decode(qz["k8"][0, 0]) * float(qz["sk"][0, 0, 0])
+    vd = e4m3_decode(qz["v8"][0, 0])
+    sv = float(qz["sv"][0, 0])
+    moved = 0
+    for i in range(N):
+        keys = np.arange(i + 1 if causal else N)
+        s = scale * (kd[keys] @ qd[i])
+        a = scale * (np.abs(kd[keys]) @ np.abs(qd[i]))
+        p = np.exp(s - s.max())
+        x = 256 * p
+        codes = e4m3_decode(e4m3_encode(x))
+        o_i = (codes / 256) @ vd[keys] * sv / p.sum()
+        np.testing.assert_allclose(o_i, o[0, 0, i], rtol=0, atol=1e-12)
+        e = s_err * (a + a.max())
+        for j in range(len(keys)):
+            for alt in (e4m3_decode(e4m3_encode(x[j] * np.exp(e[j]))),
+                        e4m3_decode(e4m3_encode(x[j] * np.exp(-e[j])))):
+                if alt == codes[j]:
+                    continue
+                moved += 1
+                c2 = codes.copy()
+                c2[j] = alt
+                o_alt = (c2 / 256) @ vd[keys] * sv / p.sum()
+                assert np.abs(o_alt - o_i).max() <= flip[0, 0, i] + 1e-12
+    assert moved > 0
