@@ -415,9 +415,12 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 // (Computing S/dP of the next tile alongside the current one was measured
 // slower than three waves per SIMD without it, at d = 64.)
 //
-// Rows past N and keys past kv_len need no mask here: their Q/dO or K/V
-// rows read as zero, so their dS (or their K row) is zero and they add
-// nothing to dQ. Only the causal diagonal is masked.
+// Rows past N need no mask: their Q and dO rows read as zero and nothing of
+// them is stored. Keys past kv_len (or past N) do: their K and V rows read
+// as zero, so s = 0 and p = exp(-LSE), which overflows for a very negative
+// LSE (fp16 already past 65504 when packing dS); 0 * inf in the dQ product
+// would then be NaN. Such keys lie only in the last tile, which is never a
+// full tile, so the mask costs the main loop nothing.
 template <int D>
 struct DqCfg {
   static constexpr int BC = 64;                    // keys per tile
@@ -599,7 +602,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
       f32x16 s_cur[KT], p_cur[KT];
       compute_sdp(par, s_cur, p_cur);
       const int t0 = tile_ix(j) * BC;
-      const bool need_mask = !FULL && a.causal && t0 + BC - 1 > wq0;
+      const bool need_mask = !FULL && ((t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0));
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -607,7 +610,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
           float p = fast_exp2(fmaf(s_cur[kt][r], sl2, -lse2));
           if (need_mask) {
             const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            p = (key <= my_q) ? p : 0.f;
+            p = (key < kv_end && (!a.causal || key <= my_q)) ? p : 0.f;
           }
           p_cur[kt][r] = p * (p_cur[kt][r] - dsum);
         }

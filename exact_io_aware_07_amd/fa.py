@@ -118,6 +118,28 @@ def _stream(stream, device) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _torch_stream(stream, device):
+    """The torch stream object of ``stream`` (None: torch's current stream;
+    a raw HIP handle is wrapped)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _temp(nbytes: int, device, stream) -> torch.Tensor:
+    """A device byte buffer the library's kernels use on ``stream``.
+
+    torch's caching allocator hands a freed block to the next allocation of
+    the stream it was allocated on, without waiting for work on other
+    streams. The buffer is therefore allocated on ``stream`` itself, so that
+    once it is dropped it is reused only behind the kernels already enqueued
+    there."""
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
 def _check_tensor(name: str, t: torch.Tensor, shape, dtype=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -176,7 +198,7 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     need = fa_bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _temp(need, q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                       _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
@@ -285,7 +307,7 @@ def fa_fwd_split(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=Non
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     need = fa_fwd_split_workspace_bytes(B, H, N, d, num_splits)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _temp(need, q.device, stream)
     if workspace is not None and not workspace.is_cuda:
         raise ValueError("workspace must be a device tensor")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -340,7 +362,7 @@ def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = F
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     need = fa_bwd_gqa_workspace_bytes(B, H, Hkv, N, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _temp(need, q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                           _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale), int(bool(causal)),
@@ -402,7 +424,7 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, block_mask, scale: float,
     sb, sh = _mask_strides(block_mask, B, H, N)
     need = fa_bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _temp(need, q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().fa_bwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
@@ -452,14 +474,16 @@ def fa_bwd_sparse_planned_workspace_bytes(B: int, H: int, N: int, d: int, counts
     return int(lib().fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, _ptr(c)))
 
 
-def _plan_args(plan: dict, device):
+def _plan_args(plan: dict, device, stream=None):
     """(device plan, CPU counts) of a plan from fa_sparse_plan. A plan whose
     "plan" tensor is already on the device is used in place; a host one is
-    copied on every call (a copy that graph capture cannot record)."""
+    copied on every call (a copy that graph capture cannot record), on the
+    stream the kernels run on, into memory allocated there (see _temp)."""
     counts = torch.as_tensor(plan["counts"], dtype=torch.int32).contiguous()
     if counts.is_cuda or counts.numel() != 8:
         raise ValueError("plan['counts'] must be the 8 host counts of fa_sparse_plan")
-    return plan["plan"].to(device=device, dtype=torch.int32).contiguous(), counts
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        return plan["plan"].to(device=device, dtype=torch.int32).contiguous(), counts
 
 
 def fa_fwd_sparse_planned(q, k, v, o, lse, block_mask, plan: dict, scale: float, causal: bool = False,
@@ -473,10 +497,10 @@ def fa_fwd_sparse_planned(q, k, v, o, lse, block_mask, plan: dict, scale: float,
     _check_tensor("o", o, q.shape)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     sb, sh = _mask_strides(block_mask, B, H, N)
-    dplan, counts = _plan_args(plan, q.device)
+    dplan, counts = _plan_args(plan, q.device, stream)
     need = fa_fwd_sparse_planned_workspace_bytes(B, H, N, d, counts)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _temp(need, q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().fa_fwd_sparse_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                      float(scale), int(bool(causal)), _kv(kv_len, B), _ptr(block_mask),
@@ -497,10 +521,10 @@ def fa_bwd_sparse_planned(q, k, v, o, dout, lse, dq, dk, dv, block_mask, plan: d
     _check_tensor("q", q, q.shape)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     sb, sh = _mask_strides(block_mask, B, H, N)
-    dplan, counts = _plan_args(plan, q.device)
+    dplan, counts = _plan_args(plan, q.device, stream)
     need = fa_bwd_sparse_planned_workspace_bytes(B, H, N, d, counts)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _temp(need, q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().fa_bwd_sparse_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
@@ -580,7 +604,7 @@ def fa_fwd_fp8_incoherent(q, k, v, signs, o, lse, scale: float, causal: bool = F
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     need = fa_fwd_fp8_workspace_bytes(B, H, N, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _temp(need, q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().fa_fwd_fp8_incoherent(_ptr(q), _ptr(k), _ptr(v), _signs(signs, d), _ptr(o),
                                      _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
@@ -599,8 +623,12 @@ def attention_forward(q, k, v, causal: bool = False, kv_len=None, scale: Optiona
                       out_dtype: Optional[torch.dtype] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     B, H, N, d = q.shape
     scale = d ** -0.5 if scale is None else scale
-    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if not q.is_cuda:
+        raise ValueError("q must be a device tensor")
+    # outputs are allocated on the stream that writes them (see _temp)
+    with torch.cuda.stream(_torch_stream(stream, q.device)):
+        o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if k.dim() == 4 and k.shape[1] != H:
         fa_fwd_gqa(q, k, v, o, lse, scale, causal, kv_len, stream)
     else:
@@ -612,7 +640,10 @@ def attention_backward(q, k, v, o, dout, lse, causal: bool = False, kv_len=None,
                        scale: Optional[float] = None, stream=None):
     d = q.shape[-1]
     scale = d ** -0.5 if scale is None else scale
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if not q.is_cuda:
+        raise ValueError("q must be a device tensor")
+    with torch.cuda.stream(_torch_stream(stream, q.device)):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if k.dim() == 4 and k.shape[1] != q.shape[1]:
         fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale, causal, kv_len, None, stream)
     else:
