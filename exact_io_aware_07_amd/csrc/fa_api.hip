@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "fa.h"
@@ -104,6 +105,29 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // difference and a row index stays inside a 32-bit int.
 constexpr int kMaxPos = 1 << 29;
 
+// Scratch of fa_bwd_noalloc: the D_i array of the backward. On the host
+// this name is a stand-in, not a device address; kernels get the address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
+
+// Per-device address of `scratch`, looked up once per device with that
+// device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(int dev, float** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,6 +177,34 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d,
                     scale, causal, stream, dtype,
                     (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float scale, int causal, const int* kv_len, void* stream, int dtype) {
+  int st = check_scalars(B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  const long long rows = (long long)B * H * N;
+  if (rows == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
+  if (rows > FA_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+    if ((int)sdev != dev) return FA_ERR_INVALID_ARG;
+  }
+  float* dsum = nullptr;
+  if (scratch_address(dev, &dsum) != hipSuccess) return FA_ERR_HIP;
+  return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, dsum, kv_len, B, H, N, d, scale, causal,
+                    stream, dtype, (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV);
 }
 
 int fa_bwd_dsum(const void* o, const void* dout, float* dsum, int B, int H, int N, int d,
@@ -658,6 +710,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128; dtype pair not supported";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or smaller than the entry point's *_workspace_bytes()";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+    case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: B*H*N exceeds FA_NOALLOC_MAX_ROWS, the built-in scratch of fa_bwd_noalloc";
     default: return "unknown fa status";
   }
 }

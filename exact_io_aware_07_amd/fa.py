@@ -17,8 +17,10 @@ from .build import LIB
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
+FA_ERR_TOO_LARGE = -5
+FA_NOALLOC_MAX_ROWS = 1 << 22  # fa_bwd_noalloc's built-in scratch, in query rows
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_dsum", "fa_bwd_dkdv",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_noalloc", "fa_bwd_dsum", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_partial", "fa_merge", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split", "fa_fwd_gqa", "fa_bwd_gqa_workspace_bytes", "fa_bwd_gqa",
            "fa_fwd_sparse", "fa_bwd_sparse", "fa_sparse_plan",
@@ -49,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp, i]
     L.fa_bwd.restype = i
+    L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
+    L.fa_bwd_noalloc.restype = i
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     L.fa_bwd_workspace_bytes.restype = sz
     L.fa_bwd_dsum.argtypes = [vp, vp, vp, i, i, i, i, vp, i]
@@ -206,6 +210,22 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False
                       _DTYPE.get(q.dtype, -99))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False,
+                   kv_len: Optional[torch.Tensor] = None, stream=None) -> None:
+    """fa_bwd with its workspace in the library's own device array (at most
+    FA_NOALLOC_MAX_ROWS = B * H * N rows); allocates nothing."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.shape, q.dtype)
+    _check_tensor("q", q, q.shape)
+    _check_tensor("lse", lse, (B, H, N), torch.float32)
+    st = lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                              _kv(kv_len, B), _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
 
 
 def fa_bwd_dsum(o, dout, dsum, stream=None) -> None:

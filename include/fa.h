@@ -62,7 +62,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, scale, flag */
   FA_ERR_UNSUPPORTED = -2, /* d not in {64,128}, or unsupported dtype pair */
   FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required */
-  FA_ERR_HIP = -4          /* the kernel launch itself failed */
+  FA_ERR_HIP = -4,         /* the kernel launch itself failed */
+  FA_ERR_TOO_LARGE = -5    /* problem exceeds fa_bwd_noalloc's built-in scratch */
 } fa_status_t;
 
 /*
@@ -128,6 +129,34 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
               const void* dout, const float* lse, float* dsum, void* dq,
               int B, int H, int N, int d, float scale, int causal,
               const int* kv_len, void* stream, int dtype);
+
+/*
+ * The backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fa_bwd without the workspace argument. Its D_i array (one fp32 per query
+ * row) lives in a fixed device array built into the library,
+ * FA_NOALLOC_MAX_ROWS floats (16 MiB), which every device the library runs
+ * on holds from the module's load until the process ends. The call
+ * allocates nothing and launches the same kernels as fa_bwd, so its
+ * results are fa_bwd's bit for bit.
+ *   Arguments, results and errors as for fa_bwd, and:
+ *   - B*H*N > FA_NOALLOC_MAX_ROWS returns FA_ERR_TOO_LARGE (nothing launched).
+ *   - stream must be NULL or a stream of the current device, else
+ *     FA_ERR_INVALID_ARG.
+ *   - The first call on a device looks the array up (hipGetSymbolAddress)
+ *     with that device current and keeps its address; a failed lookup
+ *     returns FA_ERR_HIP.
+ * Every call on one device shares that device's array and leaves its last
+ * contents there; nothing in it needs to start at any value (each call
+ * writes every D_i it reads). Calls that overlap on one device (different
+ * streams, or several host threads without ordering) race on it; calls
+ * ordered on one stream do not.
+ */
+#define FA_NOALLOC_MAX_ROWS (1 << 22)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk,
+                   void* dv, int B, int H, int N, int d, float scale, int causal,
+                   const int* kv_len, void* stream, int dtype);
 
 /*
  * Attention over part of the keys, and the merge of such parts: the pieces

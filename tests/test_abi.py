@@ -43,7 +43,8 @@ def test_library_imports_no_device_allocator():
 
 
 def test_strerror_covers_every_status():
-    for st in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_WORKSPACE, fa.FA_ERR_HIP):
+    for st in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_WORKSPACE, fa.FA_ERR_HIP,
+               fa.FA_ERR_TOO_LARGE):
         assert fa.fa_strerror(st).startswith("FA_")
     assert "unknown" in fa.fa_strerror(12345)
 
@@ -526,3 +527,34 @@ def test_autograd_wrapper_refuses_host_tensors_instead_of_computing():
     q = torch.randn(1, 1, 16, 64, dtype=torch.bfloat16, requires_grad=True)
     with pytest.raises(ValueError, match="device tensor"):
         scaled_dot_product_attention(q, q, q)
+
+
+def _bwd_noalloc(B=1, H=1, N=16, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16, q=A, dq=A, lse=A):
+    return fa.lib().fa_bwd_noalloc(q, A, A, A, A, lse, dq, A, A, B, H, N, d, scale, causal, None,
+                                   None, dtype)
+
+
+def test_noalloc_header_constant_matches_binding():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_MAX_ROWS \(1 << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == fa.FA_NOALLOC_MAX_ROWS
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    # one row past the built-in scratch: refused before any HIP call
+    (dict(B=1, H=1, N=(1 << 22) + 1), fa.FA_ERR_TOO_LARGE),
+    (dict(B=4, H=16, N=65537), fa.FA_ERR_TOO_LARGE),
+])
+def test_noalloc_backward_validation(kw, expect):
+    assert _bwd_noalloc(**kw) == expect
+
+
+def test_noalloc_backward_empty_is_ok_without_pointers():
+    assert _bwd_noalloc(N=0, q=None, dq=None, lse=None) == fa.FA_OK
