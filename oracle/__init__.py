@@ -14,4 +14,4 @@ from .gqa import attn_bwd64_gqa, attn_fwd64_gqa  # noqa: F401
 from .sparse import (attn_bwd64_sparse, attn_bwd64_sparse_sampled, attn_fwd64_sparse,  # noqa: F401
                      sparse_visible)
 from .fp8 import (E4M3_MAX, attn_fwd64_fp8, e4m3_decode, e4m3_encode, fp8_quantize,  # noqa: F401
-                  fp8_quantize_rows, fwht32)
+                  fp8_quantize_rows, fwht32, mfma_loss_bound)
