@@ -41,13 +41,18 @@ fa::Elem elem(int t) {
   return t == FA_F32 ? fa::Elem::F32 : (t == FA_F16 ? fa::Elem::F16 : fa::Elem::BF16);
 }
 
+// O in fp32 next to 16-bit inputs: the forward's fp32 output handed to the
+// backward (o_dtype == FA_F32); for fp32 inputs O is fp32 anyway.
+bool o_dtype_ok(int dtype, int o_dtype) { return o_dtype == dtype || o_dtype == FA_F32; }
+
 int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, float* dsum, const int* kv_len,
                int B, int H, int N, int d, float scale, int causal, void* stream, int dtype,
-               int stages, int Hkv = 0, int gsplit = 1, float* dkv_part = nullptr,
+               int o_dtype, int stages, int Hkv = 0, int gsplit = 1, float* dkv_part = nullptr,
                const unsigned char* bmask = nullptr, long long bm_sb = 0, long long bm_sh = 0) {
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, dsum, kv_len, B, H, N, d, scale, causal,
                 Hkv > 0 ? Hkv : H, gsplit, dkv_part, bmask, bm_sb, bm_sh};
+  a.o_f32 = (o_dtype == FA_F32 && dtype != FA_F32) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = bmask ? fa::launch_bwd_mfma_sparse(a, elem(dtype), stages, s)
                  : (dtype == FA_F32) ? fa::launch_bwd_f32(a, stages, s)
@@ -161,10 +166,11 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
            int causal, const int* kv_len, void* workspace, size_t workspace_bytes, void* stream,
-           int dtype) {
+           int dtype, int o_dtype) {
   int st = check_scalars(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!o_dtype_ok(dtype, o_dtype)) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H * N == 0) return FA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
@@ -175,16 +181,17 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
       workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
   return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d,
-                    scale, causal, stream, dtype,
+                    scale, causal, stream, dtype, o_dtype,
                     (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV);
 }
 
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                   float scale, int causal, const int* kv_len, void* stream, int dtype) {
+                   float scale, int causal, const int* kv_len, void* stream, int dtype, int o_dtype) {
   int st = check_scalars(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!o_dtype_ok(dtype, o_dtype)) return FA_ERR_UNSUPPORTED;
   const long long rows = (long long)B * H * N;
   if (rows == 0) return FA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
@@ -204,19 +211,20 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
   float* dsum = nullptr;
   if (scratch_address(dev, &dsum) != hipSuccess) return FA_ERR_HIP;
   return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, dsum, kv_len, B, H, N, d, scale, causal,
-                    stream, dtype, (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV);
+                    stream, dtype, o_dtype, (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV);
 }
 
 int fa_bwd_dsum(const void* o, const void* dout, float* dsum, int B, int H, int N, int d,
-                void* stream, int dtype) {
+                void* stream, int dtype, int o_dtype) {
   int st = check_scalars(B, H, N, d, 1.f, 0);
   if (st != FA_OK) return st;
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!o_dtype_ok(dtype, o_dtype)) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H * N == 0) return FA_OK;
   if (!o || !dout || !dsum) return FA_ERR_INVALID_ARG;
   if (!aligned16(o) || !aligned16(dout) || !aligned4(dsum)) return FA_ERR_INVALID_ARG;
   return launch_bwd(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, dsum,
-                    nullptr, B, H, N, d, 1.f, 0, stream, dtype, (int)fa::BwdStage::DSUM);
+                    nullptr, B, H, N, d, 1.f, 0, stream, dtype, o_dtype, (int)fa::BwdStage::DSUM);
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
@@ -232,15 +240,16 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
     return FA_ERR_INVALID_ARG;
   if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
   return launch_bwd(q, k, v, nullptr, dout, lse, nullptr, dk, dv, (float*)dsum, kv_len, B, H, N,
-                    d, scale, causal, stream, dtype, (int)fa::BwdStage::DKDV);
+                    d, scale, causal, stream, dtype, FA_F32, (int)fa::BwdStage::DKDV);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
               const float* lse, float* dsum, void* dq, int B, int H, int N, int d, float scale,
-              int causal, const int* kv_len, void* stream, int dtype) {
+              int causal, const int* kv_len, void* stream, int dtype, int o_dtype) {
   int st = check_scalars(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!o_dtype_ok(dtype, o_dtype)) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H * N == 0) return FA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dsum || !dq) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
@@ -248,7 +257,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const 
     return FA_ERR_INVALID_ARG;
   if (kv_len && !aligned4(kv_len)) return FA_ERR_INVALID_ARG;
   return launch_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, dsum, kv_len, B, H, N, d, scale,
-                    causal, stream, dtype, (int)fa::BwdStage::DQ);
+                    causal, stream, dtype, o_dtype, (int)fa::BwdStage::DQ);
 }
 
 int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
@@ -377,11 +386,12 @@ size_t fa_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
                float scale, int causal, const int* kv_len, void* workspace,
-               size_t workspace_bytes, void* stream, int dtype) {
+               size_t workspace_bytes, void* stream, int dtype, int o_dtype) {
   int st = check_scalars(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   if (Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!o_dtype_ok(dtype, o_dtype)) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H * N == 0) return FA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
@@ -394,7 +404,7 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
   const int gsplit = fa::bwd_group_split(B, H, Hkv, N, d);
   float* part = gsplit > 1 ? (float*)((char*)workspace + dsum_bytes_aligned(B, H, N)) : nullptr;
   return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d,
-                    scale, causal, stream, dtype,
+                    scale, causal, stream, dtype, o_dtype,
                     (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV, Hkv, gsplit, part);
 }
 
@@ -425,10 +435,11 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                   float scale, int causal, const int* kv_len, const unsigned char* block_mask,
                   long long mask_stride_b, long long mask_stride_h, void* workspace,
-                  size_t workspace_bytes, void* stream, int dtype) {
+                  size_t workspace_bytes, void* stream, int dtype, int o_dtype) {
   int st = check_scalars(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!o_dtype_ok(dtype, o_dtype)) return FA_ERR_UNSUPPORTED;
   // a mask row or column must fit the kernels' LDS list of kept blocks
   if ((N + fa::kMaskBlock - 1) / fa::kMaskBlock > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
   if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
@@ -443,7 +454,7 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
       workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
   return launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, kv_len, B, H, N, d,
-                    scale, causal, stream, dtype,
+                    scale, causal, stream, dtype, o_dtype,
                     (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV, H, 1, nullptr, block_mask,
                     mask_stride_b, mask_stride_h);
 }
@@ -591,10 +602,12 @@ int fa_bwd_sparse_planned(const void* q, const void* k, const void* v, const voi
                           int H, int N, int d, float scale, int causal, const int* kv_len,
                           const unsigned char* block_mask, long long mask_stride_b,
                           long long mask_stride_h, const int* plan, const int* counts,
-                          void* workspace, size_t workspace_bytes, void* stream, int dtype) {
+                          void* workspace, size_t workspace_bytes, void* stream, int dtype,
+                          int o_dtype) {
   int st = check_scalars(B, H, N, d, scale, causal);
   if (st != FA_OK) return st;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (!o_dtype_ok(dtype, o_dtype)) return FA_ERR_UNSUPPORTED;
   if ((N + fa::kMaskBlock - 1) / fa::kMaskBlock > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
   if (mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_INVALID_ARG;
   if ((st = check_plan(B, H, N, plan, counts)) != FA_OK) return st;
@@ -619,6 +632,7 @@ int fa_bwd_sparse_planned(const void* q, const void* k, const void* v, const voi
                 causal, H, 1, kv_part, block_mask, mask_stride_b, mask_stride_h, col_items, cols,
                 counts[0], counts[1], counts[2], row_items, rows, counts[3], counts[4], counts[5],
                 q_part};
+  a.o_f32 = o_dtype == FA_F32 ? 1 : 0;
   hipError_t e = fa::launch_bwd_mfma_sparse(a, elem(dtype),
                                             (int)fa::BwdStage::DQ | (int)fa::BwdStage::DKDV,
                                             (hipStream_t)stream);

@@ -38,29 +38,74 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------------------
+// Eight O values of one row, as fp32: elements [e0, e0 + 8) of the row
+// starting at element offset `row_off` of the head (O in the 16-bit type T,
+// or fp32 when o_f32).
+template <typename T>
+struct ORow8 {
+  float x[8];
+};
+template <typename T>
+__device__ inline ORow8<T> load_o8(__amdgpu_buffer_rsrc_t r, uint32_t elem_off, bool o_f32) {
+  ORow8<T> v;
+  if (o_f32) {
+    const f32x4 a = __builtin_bit_cast(f32x4, buf_load16(r, elem_off * 4));
+    const f32x4 b = __builtin_bit_cast(f32x4, buf_load16(r, elem_off * 4 + 16));
+    v.x[0] = a[0];
+    v.x[1] = a[1];
+    v.x[2] = a[2];
+    v.x[3] = a[3];
+    v.x[4] = b[0];
+    v.x[5] = b[1];
+    v.x[6] = b[2];
+    v.x[7] = b[3];
+  } else {
+    const u32x4 a = buf_load16(r, elem_off * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v.x[2 * i] = Mfma<T>::to_f32(a[i] & 0xffffu);
+      v.x[2 * i + 1] = Mfma<T>::to_f32(a[i] >> 16);
+    }
+  }
+  return v;
+}
+
+// sum_e o[e] * g[e] over one 8-element chunk, in element order, onto acc
+// (g: the matching 8 dO values, 16-bit, in a u32x4).
+template <typename T>
+__device__ inline float dot8(const ORow8<T>& o, u32x4 g, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(o.x[2 * i], Mfma<T>::to_f32(g[i] & 0xffffu), acc);
+    acc = fmaf(o.x[2 * i + 1], Mfma<T>::to_f32(g[i] >> 16), acc);
+  }
+  return acc;
+}
+
 // D_i = sum_c dO_ic O_ic (fp32), in the order the dQ kernel forms it (two
 // lanes per row; lane h sums the 8-element chunks 16 c + 8 h, c = 0, 1, ...,
 // in turn; then the two halves are added), so that D, and a backward run as
 // D, dK/dV and dQ stages, equal the one-call backward bit for bit.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void dsum_kernel(const uint16_t* __restrict__ o,
+__global__ __launch_bounds__(256) void dsum_kernel(const void* __restrict__ o,
                                                    const uint16_t* __restrict__ dout,
-                                                   float* __restrict__ dsum, long rows) {
+                                                   float* __restrict__ dsum, long rows, int o_f32) {
   constexpr int RPB = 128;  // rows per workgroup
   const int tid = threadIdx.x;
-  const long row = (long)blockIdx.x * RPB + tid / 2;
+  const long row0 = (long)blockIdx.x * RPB;
+  const long row = row0 + tid / 2;
   const int h = tid & 1;
+  // this workgroup's rows of O as a buffer (32-bit offsets inside it)
+  const long nrows = min((long)RPB, rows - row0);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+      (const unsigned char*)o + row0 * D * (o_f32 ? 4 : 2), (uint32_t)(nrows * D * (o_f32 ? 4 : 2)));
   float acc = 0.f;
   if (row < rows) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const u32x4 ov = *(const u32x4*)(o + row * D + c * 16 + h * 8);
+      const ORow8<T> ov = load_o8<T>(ro, (uint32_t)((row - row0) * D + c * 16 + h * 8), o_f32 != 0);
       const u32x4 gv = *(const u32x4*)(dout + row * D + c * 16 + h * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc = fmaf(Mfma<T>::to_f32(ov[i] & 0xffffu), Mfma<T>::to_f32(gv[i] & 0xffffu), acc);
-        acc = fmaf(Mfma<T>::to_f32(ov[i] >> 16), Mfma<T>::to_f32(gv[i] >> 16), acc);
-      }
+      acc = dot8<T>(ov, gv, acc);
     }
   }
   acc += __shfl_xor(acc, 1, 64);
@@ -527,24 +572,41 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   // already in VGPRs and the matching O fragments (this half of the wave
   // holds half of the row; the halves are summed). Written to the workspace
   // for the dK/dV kernel, which runs after this one.
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const uint16_t*)a.o + head_off, (uint32_t)N * D * 2);
+  const int ob = a.o_f32 ? 4 : 2;  // bytes per O element
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc((const unsigned char*)a.o + head_off * ob, (uint32_t)N * D * ob);
   float dsum = 0.f;
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) {
-    const u32x4 of = buf_load16(ro, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dsum = fmaf(Mfma<T>::to_f32(of[i] & 0xffffu), Mfma<T>::to_f32(gf[dc][i] & 0xffffu), dsum);
-      dsum = fmaf(Mfma<T>::to_f32(of[i] >> 16), Mfma<T>::to_f32(gf[dc][i] >> 16), dsum);
-    }
+    const ORow8<T> of = load_o8<T>(ro, (uint32_t)(my_q * D + dc * 16 + hh * 8), a.o_f32 != 0);
+    dsum = dot8<T>(of, gf[dc], dsum);
   }
   dsum = halves_sum(dsum);
+  // A wave whose rows see one key tile in all forms D_i exactly from that
+  // tile instead, as sum_j P_ij dP_ij over the P and dP it computes (the
+  // definition of D that rowsum(dO * O) equals in exact arithmetic), so
+  // that O's rounding, which the stored O carries, does not enter dS =
+  // P (dP - D). On rows of one or two visible keys that difference is of
+  // nearly equal terms and O's rounding would dominate it. Not for rows cut
+  // into pieces (a piece sees only part of the row).
+  // Tiles that no row of the workgroup sees only partly (causal) form the
+  // main loop; a full tile also loads the next one unconditionally, so it
+  // must not be the last.
+  int n_full = a.causal ? (q_blk0 + 1) / BC : ntiles;
+  if constexpr (SP) {
+    if (a.causal) n_full = mask_tiles_below(plist, n_kept, n_full);
+  }
+  n_full = min(n_full, ntiles - 1);
+  // (a wave with one tile runs it as a partial tile: n_full is then 0; a
+  // row item with slot < 0 is a whole row, not cut)
+  const bool whole_row = !by_items || slot < 0;
+  const bool single = (w_tiles == 1) && whole_row && n_full <= 0;
   float lse2 = 0.f;
   if (my_q < N) {
     const float l = a.lse[(size_t)bh * N + my_q];
     lse2 = (l == -INFINITY) ? 0.f : l * kLog2e;
     // every piece of a row forms the same D_i; the first one stores it
-    if (hh == 0 && piece0 == 0) a.dsum[(size_t)bh * N + my_q] = dsum;
+    if (hh == 0 && piece0 == 0 && !single) a.dsum[(size_t)bh * N + my_q] = dsum;
   }
   const float sl2 = a.scale * kLog2e;
 
@@ -583,6 +645,30 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
     load_k(0, 0);
     load_v(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
+  }
+  // Waves whose rows see one tile: D_i = sum_j P_ij dP_ij over that tile
+  // (see `single`), from the same S and dP the tile pass recomputes bit for
+  // bit. Only workgroups of at most two tiles can hold such a wave, so the
+  // extra barrier is confined to them.
+  if (ntiles > 0 && ntiles <= 2 && whole_row) {
+    __syncthreads();
+    if (single) {
+      f32x16 s0[KT], dp0[KT];
+      compute_sdp(0, s0, dp0);
+      const int t0 = tile_ix(0) * BC;
+      float acc = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s0[kt][r], sl2, -lse2));
+          const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          acc = fmaf((key < kv_end && (!a.causal || key <= my_q)) ? p : 0.f, dp0[kt][r], acc);
+        }
+      }
+      dsum = halves_sum(acc);
+      if (hh == 0 && my_q < N) a.dsum[(size_t)bh * N + my_q] = dsum;
+    }
   }
 
   // Tile j: S^T/dP^T, then dS and dQ. Full tiles (no causal mask for any
@@ -636,14 +722,6 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
 
   using Full = std::integral_constant<bool, true>;
   using Part = std::integral_constant<bool, false>;
-  // Tiles that no row of the workgroup sees only partly (causal) form the
-  // main loop; a full tile also loads the next one unconditionally, so it
-  // must not be the last.
-  int n_full = a.causal ? (q_blk0 + 1) / BC : ntiles;
-  if constexpr (SP) {
-    if (a.causal) n_full = mask_tiles_below(plist, n_kept, n_full);
-  }
-  n_full = min(n_full, ntiles - 1);
   int j = 0;
   for (; j + 1 < n_full; j += 2) {
     tile(j, Full{}, 0);
@@ -771,7 +849,7 @@ hipError_t launch(const BwdArgs& a, int stages, hipStream_t st) {
     const long rows = (long)a.B * a.H * a.N;
     constexpr int RPB = 128;
     hipLaunchKernelGGL((dsum_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       st, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.dsum, rows);
+                       st, a.o, (const uint16_t*)a.dout, a.dsum, rows, a.o_f32);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & (int)BwdStage::DQ) {

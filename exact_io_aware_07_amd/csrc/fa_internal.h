@@ -93,6 +93,9 @@ struct BwdArgs {
   const int* sq_rows;
   int sq_nitems, sq_nrows, sq_nslots;
   float* sq_part;
+  // O is fp32 (the forward's fp32 output) rather than the 16-bit input type:
+  // D_i is then formed without O's 16-bit rounding.
+  int o_f32;
 };
 
 // Blocks per piece of a block-sparse mask row or column.

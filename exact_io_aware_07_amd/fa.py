@@ -49,17 +49,17 @@ def lib() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, i]
     L.fa_fwd.restype = i
-    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp, i]
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp, i, i]
     L.fa_bwd.restype = i
-    L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
+    L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, i]
     L.fa_bwd_noalloc.restype = i
     L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     L.fa_bwd_workspace_bytes.restype = sz
-    L.fa_bwd_dsum.argtypes = [vp, vp, vp, i, i, i, i, vp, i]
+    L.fa_bwd_dsum.argtypes = [vp, vp, vp, i, i, i, i, vp, i, i]
     L.fa_bwd_dsum.restype = i
     L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
     L.fa_bwd_dkdv.restype = i
-    L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i]
+    L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, i]
     L.fa_bwd_dq.restype = i
     L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, vp, i]
     L.fa_fwd_partial.restype = i
@@ -74,13 +74,13 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_bwd_gqa_workspace_bytes.restype = sz
     L.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz,
-                             vp, i]
+                             vp, i, i]
     L.fa_bwd_gqa.restype = i
     ll = ctypes.c_longlong
     L.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, ll, ll, vp, i, i]
     L.fa_fwd_sparse.restype = i
     L.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, ll,
-                                ll, vp, sz, vp, i]
+                                ll, vp, sz, vp, i, i]
     L.fa_bwd_sparse.restype = i
     L.fa_sparse_plan.argtypes = [vp, ll, ll, i, i, i, i, vp, ll, vp]
     L.fa_sparse_plan.restype = i
@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_sparse_planned_workspace_bytes.argtypes = [i, i, i, i, vp]
     L.fa_bwd_sparse_planned_workspace_bytes.restype = sz
     L.fa_bwd_sparse_planned.argtypes = ([vp] * 9 + [i, i, i, i, f, i, vp, vp, ll, ll, vp, vp, vp, sz,
-                                                     vp, i])
+                                                     vp, i, i])
     L.fa_bwd_sparse_planned.restype = i
     L.fa_fp8_quantize.argtypes = [vp] * 11 + [i, i, i, i, vp, i]
     L.fa_fp8_quantize.restype = i
@@ -155,6 +155,15 @@ def _check_tensor(name: str, t: torch.Tensor, shape, dtype=None):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def _check_o(o: torch.Tensor, q: torch.Tensor) -> int:
+    """O for a backward: q's shape, in q's dtype or fp32 (the forward's fp32
+    output); returns its dtype code."""
+    _check_tensor("o", o, q.shape)
+    if o.dtype not in (q.dtype, torch.float32):
+        raise ValueError(f"o has dtype {o.dtype}, expected {q.dtype} or torch.float32")
+    return _DTYPE[o.dtype]
+
+
 def _kv(kv_len: Optional[torch.Tensor], B: int) -> Optional[int]:
     if kv_len is None:
         return None
@@ -196,9 +205,10 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False
     bytes (allocated here when None).
     """
     B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype)
     _check_tensor("q", q, q.shape)
+    o_dt = _check_o(o, q)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     need = fa_bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
@@ -207,7 +217,7 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = False
     st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                       _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                       _kv(kv_len, B), _ptr(workspace), ws_bytes, _stream(stream, q.device),
-                      _DTYPE.get(q.dtype, -99))
+                      _DTYPE.get(q.dtype, -99), o_dt)
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
 
@@ -217,25 +227,27 @@ def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool
     """fa_bwd with its workspace in the library's own device array (at most
     FA_NOALLOC_MAX_ROWS = B * H * N rows); allocates nothing."""
     B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype)
     _check_tensor("q", q, q.shape)
+    o_dt = _check_o(o, q)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     st = lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                               _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
-                              _kv(kv_len, B), _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+                              _kv(kv_len, B), _stream(stream, q.device), _DTYPE.get(q.dtype, -99), o_dt)
     if st != FA_OK:
         raise FaError(st, "fa_bwd_noalloc")
 
 
 def fa_bwd_dsum(o, dout, dsum, stream=None) -> None:
-    """D_i alone: dsum[b, h, i] = sum_c dout * o (fp32 [B, H, N])."""
+    """D_i alone: dsum[b, h, i] = sum_c dout * o (fp32 [B, H, N]); o in
+    dout's dtype or fp32."""
     B, H, N, d = o.shape
-    _check_tensor("o", o, o.shape)
-    _check_tensor("dout", dout, o.shape, o.dtype)
+    _check_tensor("dout", dout, o.shape)
+    o_dt = _check_o(o, dout)
     _check_tensor("dsum", dsum, (B, H, N), torch.float32)
     st = lib().fa_bwd_dsum(_ptr(o), _ptr(dout), _ptr(dsum), B, H, N, d, _stream(stream, o.device),
-                           _DTYPE.get(o.dtype, -99))
+                           _DTYPE.get(dout.dtype, -99), o_dt)
     if st != FA_OK:
         raise FaError(st, "fa_bwd_dsum")
 
@@ -260,14 +272,15 @@ def fa_bwd_dq(q, k, v, o, dout, lse, dsum, dq, scale: float, causal: bool = Fals
               kv_len: Optional[torch.Tensor] = None, stream=None) -> None:
     """Backward stage: writes dq and dsum (D_i = rowsum(dout * o), fp32 [B, H, N])."""
     B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)):
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq)):
         _check_tensor(name, t, q.shape, q.dtype)
     _check_tensor("q", q, q.shape)
+    o_dt = _check_o(o, q)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     _check_tensor("dsum", dsum, (B, H, N), torch.float32)
     st = lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dsum),
                          _ptr(dq), B, H, N, d, float(scale), int(bool(causal)), _kv(kv_len, B),
-                         _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+                         _stream(stream, q.device), _DTYPE.get(q.dtype, -99), o_dt)
     if st != FA_OK:
         raise FaError(st, "fa_bwd_dq")
 
@@ -374,8 +387,9 @@ def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = F
     """Enqueue the grouped-query backward: dq [B, H, N, d]; dk, dv
     [B, Hkv, N, d], each the sum over the K/V head's query heads."""
     B, H, Hkv, N, d = _gqa_shapes(q, k)
-    for name, t in (("o", o), ("dout", dout), ("dq", dq)):
+    for name, t in (("dout", dout), ("dq", dq)):
         _check_tensor(name, t, q.shape, q.dtype)
+    o_dt = _check_o(o, q)
     for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, (B, Hkv, N, d), q.dtype)
     _check_tensor("q", q, q.shape)
@@ -387,7 +401,7 @@ def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool = F
     st = lib().fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                           _ptr(dk), _ptr(dv), B, H, Hkv, N, d, float(scale), int(bool(causal)),
                           _kv(kv_len, B), _ptr(workspace), ws_bytes, _stream(stream, q.device),
-                          _DTYPE.get(q.dtype, -99))
+                          _DTYPE.get(q.dtype, -99), o_dt)
     if st != FA_OK:
         raise FaError(st, "fa_bwd_gqa")
 
@@ -437,9 +451,10 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, block_mask, scale: float,
                   causal: bool = False, kv_len=None, workspace=None, stream=None) -> None:
     """Enqueue the block-sparse backward (gradients of fa_fwd_sparse's output)."""
     B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype)
     _check_tensor("q", q, q.shape)
+    o_dt = _check_o(o, q)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     sb, sh = _mask_strides(block_mask, B, H, N)
     need = fa_bwd_workspace_bytes(B, H, N, d)
@@ -449,7 +464,7 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, block_mask, scale: float,
     st = lib().fa_bwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                              _kv(kv_len, B), _ptr(block_mask), sb, sh, _ptr(workspace), ws_bytes,
-                             _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+                             _stream(stream, q.device), _DTYPE.get(q.dtype, -99), o_dt)
     if st != FA_OK:
         raise FaError(st, "fa_bwd_sparse")
 
@@ -536,9 +551,10 @@ def fa_bwd_sparse_planned(q, k, v, o, dout, lse, dq, dk, dv, block_mask, plan: d
     """fa_bwd_sparse with the plan of fa_sparse_plan (long mask columns and
     rows cut into pieces whose fp32 partials are added in order)."""
     B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, q.shape, q.dtype)
     _check_tensor("q", q, q.shape)
+    o_dt = _check_o(o, q)
     _check_tensor("lse", lse, (B, H, N), torch.float32)
     sb, sh = _mask_strides(block_mask, B, H, N)
     dplan, counts = _plan_args(plan, q.device, stream)
@@ -550,7 +566,7 @@ def fa_bwd_sparse_planned(q, k, v, o, dout, lse, dq, dk, dv, block_mask, plan: d
                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
                                      int(bool(causal)), _kv(kv_len, B), _ptr(block_mask), sb, sh,
                                      _ptr(dplan), _ptr(counts), _ptr(workspace), ws_bytes,
-                                     _stream(stream, q.device), _DTYPE.get(q.dtype, -99))
+                                     _stream(stream, q.device), _DTYPE.get(q.dtype, -99), o_dt)
     if st != FA_OK:
         raise FaError(st, "fa_bwd_sparse_planned")
 

@@ -90,19 +90,28 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
  * Backward: dQ, dK, dV of L = sum(dO * O) for the forward above.
- *   q, k, v, o, dout  [B,H,N,d] in dtype; o is the forward's output.
+ *   q, k, v, dout     [B,H,N,d] in dtype.
+ *   o                 [B,H,N,d] in o_dtype: dtype, or FA_F32 for 16-bit
+ *                     inputs: the forward's output, in the type it was
+ *                     written in. The backward forms D_i = sum_c dO_ic O_ic
+ *                     from it, so an fp32 O keeps O's 16-bit rounding out
+ *                     of D; that rounding is what limits dQ and dK on rows
+ *                     with one or two visible keys, where dS = P (dP - D)
+ *                     is a difference of nearly equal terms. Other o_dtype
+ *                     values return FA_ERR_UNSUPPORTED.
  *   lse               [B,H,N] fp32 from fa_fwd with the same arguments.
  *   dq, dk, dv        [B,H,N,d] in dtype (written, not accumulated).
  *   workspace         device buffer of at least fa_bwd_workspace_bytes(),
  *                     16-byte aligned, owned by the caller; its contents on
- *                     entry are ignored.
+ *                     entry are ignored. It receives D_i (see fa_bwd_dsum
+ *                     below for how D_i is formed).
  * Deterministic: the same inputs give bit-identical gradients.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal,
            const int* kv_len, void* workspace, size_t workspace_bytes,
-           void* stream, int dtype);
+           void* stream, int dtype, int o_dtype);
 
 /*
  * The backward as its stages, for callers that want to time them. fa_bwd
@@ -113,14 +122,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *                D_i for its own rows; dsum 4-byte aligned).
  *   fa_bwd_dkdv: reads q, k, v, dout, lse, dsum; writes dk, dv. dsum must
  *                hold D_i, from fa_bwd_dq or fa_bwd_dsum, before it runs.
- *   fa_bwd_dsum: reads o, dout; writes dsum. The same D_i on its own, for a
- *                caller that wants dK/dV without dQ. It sums in the order
- *                fa_bwd_dq does, so either order of stages gives fa_bwd's
- *                dsum, dq, dk and dv bit for bit.
+ *   fa_bwd_dsum: reads o, dout; writes dsum. D_i = rowsum(dO * O) on its
+ *                own, for a caller that wants dK/dV without dQ. It sums in
+ *                the order fa_bwd_dq does, so on every row that sees more
+ *                than one 64-key tile either order of stages gives fa_bwd's
+ *                bits. On a row whose visible keys lie in one 64-key tile
+ *                fa_bwd_dq forms D_i instead as sum_j P_ij dP_ij from the P
+ *                and dP it computes (equal in exact arithmetic, and free of
+ *                O's rounding, which dominates dS = P (dP - D) on rows of
+ *                one or two keys); fa_bwd_dsum cannot, having no Q, K, V.
  * Errors as for fa_bwd (no FA_ERR_WORKSPACE: dsum is a plain argument).
  */
 int fa_bwd_dsum(const void* o, const void* dout, float* dsum, int B, int H,
-                int N, int d, void* stream, int dtype);
+                int N, int d, void* stream, int dtype, int o_dtype);
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                 const float* lse, const float* dsum, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal,
@@ -128,7 +142,7 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
               const void* dout, const float* lse, float* dsum, void* dq,
               int B, int H, int N, int d, float scale, int causal,
-              const int* kv_len, void* stream, int dtype);
+              const int* kv_len, void* stream, int dtype, int o_dtype);
 
 /*
  * The backward for callers that cannot allocate device memory (code under
@@ -156,7 +170,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o,
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk,
                    void* dv, int B, int H, int N, int d, float scale, int causal,
-                   const int* kv_len, void* stream, int dtype);
+                   const int* kv_len, void* stream, int dtype, int o_dtype);
 
 /*
  * Attention over part of the keys, and the merge of such parts: the pieces
@@ -242,7 +256,7 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                const void* dout, const float* lse, void* dq, void* dk, void* dv,
                int B, int H, int Hkv, int N, int d, float scale, int causal,
                const int* kv_len, void* workspace, size_t workspace_bytes,
-               void* stream, int dtype);
+               void* stream, int dtype, int o_dtype);
 
 /*
  * Block-sparse attention: attention restricted to the (query block, key
@@ -275,7 +289,7 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o,
                   int B, int H, int N, int d, float scale, int causal,
                   const int* kv_len, const unsigned char* block_mask,
                   long long mask_stride_b, long long mask_stride_h, void* workspace,
-                  size_t workspace_bytes, void* stream, int dtype);
+                  size_t workspace_bytes, void* stream, int dtype, int o_dtype);
 
 /*
  * Block-sparse attention with long mask lines cut into pieces. In
@@ -325,7 +339,7 @@ int fa_bwd_sparse_planned(const void* q, const void* k, const void* v, const voi
                           const int* kv_len, const unsigned char* block_mask,
                           long long mask_stride_b, long long mask_stride_h,
                           const int* plan, const int* counts, void* workspace,
-                          size_t workspace_bytes, void* stream, int dtype);
+                          size_t workspace_bytes, void* stream, int dtype, int o_dtype);
 
 /*
  * FP8 forward with incoherent processing (marketmaker.cc article, section

@@ -34,7 +34,8 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["attn_fwd64", "attn_probs64", "attn_bwd64", "attn_bwd64_sampled", "visible_mask"]
+__all__ = ["attn_fwd64", "attn_probs64", "attn_bwd64", "attn_bwd64_magnitudes", "attn_bwd64_sampled",
+           "visible_mask"]
 
 
 def _f64(x) -> np.ndarray:
@@ -161,6 +162,33 @@ def attn_bwd64(q, k, v, dout, scale: float, causal: bool = False, kv_len=None,
     if heads is None:
         return (dq.reshape(B, H, N, d), dk.reshape(B, H, N, d), dv.reshape(B, H, N, d))
     return dq, dk, dv
+
+
+def attn_bwd64_magnitudes(q, k, v, dout, scale: float, causal: bool = False, kv_len=None):
+    """The gradient formulas of ``attn_bwd64`` with every term in absolute
+    value, the scale of rounding in a floating-point evaluation of them:
+      M_dQ = scale (P * (|dP| + |D|)) |K|,  M_dK = scale (P * (|dP| + |D|))^T |Q|,
+      M_dV = P^T |dO|.
+    Each bounds its gradient elementwise (|dQ| <= M_dQ, ...). Where the terms
+    nearly cancel (a row of one or two keys with nearly equal dP), the
+    gradient is far smaller than M and a relative error bound on it alone is
+    out of reach of any fp32 evaluation. Returns three [B, H, N, d] arrays."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    lens = _kv_lens(kv_len, B, N)
+    mq, mk, mv = (np.zeros((B, H, N, d)) for _ in range(3))
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            _, _, p = _rows_forward(q[b, h], k[b, h], v[b, h], rows, scale, causal, int(lens[b]))
+            do = dout[b, h]
+            dp = do @ v[b, h].T
+            dsum = (p * dp).sum(axis=1, keepdims=True)
+            w = p * (np.abs(dp) + np.abs(dsum))
+            mq[b, h] = scale * (w @ np.abs(k[b, h]))
+            mk[b, h] = scale * (w.T @ np.abs(q[b, h]))
+            mv[b, h] = p.T @ np.abs(do)
+    return mq, mk, mv
 
 
 def attn_bwd64_sampled(q, k, v, dout, scale: float, causal: bool = False, kv_len=None,

@@ -55,9 +55,9 @@ def _fwd(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=16, d=64, scale=0.125, causal=0,
 
 
 def _bwd(ws=A, ws_bytes=1 << 20, B=1, H=1, N=16, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16,
-         q=A, dq=A):
+         q=A, dq=A, ot=None):
     return fa.lib().fa_bwd(q, A, A, A, A, A, dq, A, A, B, H, N, d, scale, causal, None, ws,
-                           ws_bytes, None, dtype)
+                           ws_bytes, None, dtype, dtype if ot is None else ot)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -100,6 +100,9 @@ def test_empty_forward_and_backward_are_ok_without_pointers(kw):
     (dict(d=48), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
     (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(ot=fa.FA_F16), fa.FA_ERR_UNSUPPORTED),                   # O neither bf16 nor fp32
+    (dict(dtype=fa.FA_F32, ot=fa.FA_BF16), fa.FA_ERR_UNSUPPORTED),
+    (dict(ot=fa.FA_F32, ws=None), fa.FA_ERR_WORKSPACE),            # fp32 O accepted, then checks go on
 ])
 def test_backward_validation(kw, expect):
     assert _bwd(**kw) == expect
@@ -129,21 +132,26 @@ def test_package_never_imports_the_oracle():
 
 def test_stage_entry_points_validate_before_launch():
     L = fa.lib()
-    assert L.fa_bwd_dsum(None, A, A, 1, 1, 16, 64, None, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_bwd_dsum(A, A, A + 2, 1, 1, 16, 64, None, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_bwd_dsum(A, A, A, 1, 1, 16, 80, None, fa.FA_BF16) == fa.FA_ERR_UNSUPPORTED
-    assert L.fa_bwd_dsum(None, None, None, 0, 1, 16, 64, None, fa.FA_BF16) == fa.FA_OK
+    bf = fa.FA_BF16
+    assert L.fa_bwd_dsum(None, A, A, 1, 1, 16, 64, None, bf, bf) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dsum(A, A, A + 2, 1, 1, 16, 64, None, bf, bf) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dsum(A, A, A, 1, 1, 16, 80, None, bf, bf) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_bwd_dsum(A, A, A, 1, 1, 16, 64, None, bf, fa.FA_F16) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_bwd_dsum(None, None, None, 0, 1, 16, 64, None, bf, bf) == fa.FA_OK
+    assert L.fa_bwd_dsum(None, None, None, 0, 1, 16, 64, None, bf, fa.FA_F32) == fa.FA_OK
     assert L.fa_bwd_dkdv(A, A, A, A, A, None, A, A, 1, 1, 16, 64, 0.125, 0, None, None,
                          fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
     assert L.fa_bwd_dkdv(A, A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 3, None, None,
                          fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
     assert L.fa_bwd_dq(A, A, A, A, A, A, A, None, 1, 1, 16, 64, 0.125, 0, None, None,
-                       fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+                       bf, bf) == fa.FA_ERR_INVALID_ARG
     assert L.fa_bwd_dq(A, A, A, None, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None,
-                       fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
+                       bf, fa.FA_F32) == fa.FA_ERR_INVALID_ARG
     assert L.fa_bwd_dq(A, A, A, A, A, A, A + 2, A, 1, 1, 16, 64, 0.125, 0, None, None,
-                       fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_bwd_dq(A, A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None, 9) == fa.FA_ERR_UNSUPPORTED
+                       bf, bf) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dq(A, A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None, 9, 9) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_bwd_dq(A, A, A, A, A, A, A, A, 1, 1, 16, 64, 0.125, 0, None, None, bf,
+                       fa.FA_F16) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_sequence_longer_than_a_32_bit_head_is_unsupported():
@@ -247,7 +255,7 @@ def _fwd_gqa(q=A, k=A, v=A, o=A, lse=A, B=1, H=4, Hkv=2, N=16, d=64, scale=0.125
 def _bwd_gqa(ws=A, ws_bytes=1 << 20, B=1, H=4, Hkv=2, N=16, d=64, scale=0.125, causal=0,
              dtype=fa.FA_BF16, dk=A):
     return fa.lib().fa_bwd_gqa(A, A, A, A, A, A, A, dk, A, B, H, Hkv, N, d, scale, causal, None,
-                               ws, ws_bytes, None, dtype)
+                               ws, ws_bytes, None, dtype, dtype)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -284,7 +292,7 @@ def test_gqa_empty_calls_are_ok_without_pointers():
     assert L.fa_fwd_gqa(None, None, None, None, None, 1, 4, 2, 0, 64, 0.125, 0, None, None,
                         fa.FA_BF16, fa.FA_BF16) == fa.FA_OK
     assert L.fa_bwd_gqa(None, None, None, None, None, None, None, None, None, 0, 4, 2, 16, 64,
-                        0.125, 0, None, None, 0, None, fa.FA_BF16) == fa.FA_OK
+                        0.125, 0, None, None, 0, None, fa.FA_BF16, fa.FA_BF16) == fa.FA_OK
     # the head counts are checked even when there is nothing to compute
     assert L.fa_fwd_gqa(None, None, None, None, None, 1, 4, 3, 0, 64, 0.125, 0, None, None,
                         fa.FA_BF16, fa.FA_BF16) == fa.FA_ERR_INVALID_ARG
@@ -314,7 +322,7 @@ def _fwd_sp(q=A, mask=A, B=1, H=2, N=300, d=64, sb=0, sh=9, causal=0, it=fa.FA_B
 
 def _bwd_sp(mask=A, ws=A, ws_bytes=1 << 20, B=1, H=2, N=300, d=64, sb=0, sh=9, dtype=fa.FA_BF16):
     return fa.lib().fa_bwd_sparse(A, A, A, A, A, A, A, A, A, B, H, N, d, 0.125, 0, None, mask, sb,
-                                  sh, ws, ws_bytes, None, dtype)
+                                  sh, ws, ws_bytes, None, dtype, dtype)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -347,7 +355,7 @@ def test_sparse_empty_calls_need_no_pointers():
     assert L.fa_fwd_sparse(None, None, None, None, None, 0, 2, 300, 64, 0.125, 0, None, None, 0, 0,
                            None, fa.FA_BF16, fa.FA_BF16) == fa.FA_OK
     assert L.fa_bwd_sparse(None, None, None, None, None, None, None, None, None, 1, 2, 0, 64, 0.125,
-                           0, None, None, 0, 0, None, 0, None, fa.FA_BF16) == fa.FA_OK
+                           0, None, None, 0, 0, None, 0, None, fa.FA_BF16, fa.FA_F32) == fa.FA_OK
 
 
 def test_fp8_validation():
@@ -501,7 +509,7 @@ def test_sparse_planned_validation():
         counts, A, ws, None, fa.FA_BF16, fa.FA_BF16)
     bwd = lambda counts, ws=1 << 20, **kw: L.fa_bwd_sparse_planned(
         *([A] * 9), 1, 2, 300, 64, 0.125, 0, None, kw.get("mask", A), 0, 0, kw.get("plan", A), counts,
-        A, ws, None, fa.FA_BF16)
+        A, ws, None, fa.FA_BF16, fa.FA_BF16)
     for f in (fwd, bwd):
         assert f(C(5, 0, 0, 6, 0, 0, 0, 0)) == fa.FA_ERR_INVALID_ARG       # too few column items
         assert f(C(6, 0, 0, 5, 0, 0, 0, 0)) == fa.FA_ERR_INVALID_ARG       # too few row items
@@ -519,7 +527,8 @@ def test_sparse_planned_validation():
                                    0, None, C(0, 0, 0, 0, 0, 0, 0, 0), None, 0, None, fa.FA_BF16,
                                    fa.FA_BF16) == fa.FA_OK
     assert L.fa_bwd_sparse_planned(*([None] * 9), 1, 2, 0, 64, 0.125, 0, None, None, 0, 0, None,
-                                   C(0, 0, 0, 0, 0, 0, 0, 0), None, 0, None, fa.FA_BF16) == fa.FA_OK
+                                   C(0, 0, 0, 0, 0, 0, 0, 0), None, 0, None, fa.FA_BF16,
+                                   fa.FA_BF16) == fa.FA_OK
 
 
 def test_autograd_wrapper_refuses_host_tensors_instead_of_computing():
@@ -531,7 +540,7 @@ def test_autograd_wrapper_refuses_host_tensors_instead_of_computing():
 
 def _bwd_noalloc(B=1, H=1, N=16, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16, q=A, dq=A, lse=A):
     return fa.lib().fa_bwd_noalloc(q, A, A, A, A, lse, dq, A, A, B, H, N, d, scale, causal, None,
-                                   None, dtype)
+                                   None, dtype, dtype)
 
 
 def test_noalloc_header_constant_matches_binding():

@@ -307,3 +307,40 @@ def test_sampled_backward_of_late_keys_under_the_causal_mask():
                                    row_chunk=8)
     np.testing.assert_allclose(sk[0], dk[0, 0, keys], rtol=0, atol=1e-12)
     np.testing.assert_allclose(sv[0], dv[0, 0, keys], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_magnitudes_by_explicit_loops_and_as_bounds(causal):
+    """attn_bwd64_magnitudes against the same formulas written as loops with
+    math.exp (N = 5), as elementwise bounds of the gradients on random
+    inputs, and equal to dV where dO >= 0."""
+    from oracle import attn_bwd64_magnitudes
+    rng = np.random.default_rng(21 + causal)
+    B, H, N, d, scale = 1, 1, 5, 3, 0.7
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    mq, mk, mv = attn_bwd64_magnitudes(q, k, v, do, scale, causal)
+    Q, K, V, G = q[0, 0], k[0, 0], v[0, 0], do[0, 0]
+    P = [[0.0] * N for _ in range(N)]
+    for i in range(N):
+        keys = [j for j in range(N) if not (causal and j > i)]
+        s = {j: scale * sum(Q[i][c] * K[j][c] for c in range(d)) for j in keys}
+        mx = max(s.values())
+        z = math.fsum(math.exp(s[j] - mx) for j in keys)
+        for j in keys:
+            P[i][j] = math.exp(s[j] - mx) / z
+    dP = [[sum(G[i][c] * V[j][c] for c in range(d)) for j in range(N)] for i in range(N)]
+    D = [math.fsum(P[i][j] * dP[i][j] for j in range(N)) for i in range(N)]
+    W = [[P[i][j] * (abs(dP[i][j]) + abs(D[i])) for j in range(N)] for i in range(N)]
+    for i in range(N):
+        for c in range(d):
+            assert abs(mq[0, 0, i, c] - scale * math.fsum(W[i][j] * abs(K[j][c]) for j in range(N))) < 1e-12
+            assert abs(mk[0, 0, i, c] - scale * math.fsum(W[j][i] * abs(Q[j][c]) for j in range(N))) < 1e-12
+            assert abs(mv[0, 0, i, c] - math.fsum(P[j][i] * abs(G[j][c]) for j in range(N))) < 1e-12
+    q, k, v, do = (rng.standard_normal((2, 2, 40, 8)) for _ in range(4))
+    grads = attn_bwd64(q, k, v, do, 0.3, causal, [40, 17])
+    mags = attn_bwd64_magnitudes(q, k, v, do, 0.3, causal, [40, 17])
+    for g, m in zip(grads, mags):
+        assert np.all(np.abs(g) <= m + 1e-12)
+    dv = attn_bwd64(q, k, v, np.abs(do), 0.3, causal)[2]
+    np.testing.assert_allclose(attn_bwd64_magnitudes(q, k, v, np.abs(do), 0.3, causal)[2], dv,
+                               rtol=0, atol=1e-12)
