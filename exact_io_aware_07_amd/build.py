@@ -69,5 +69,54 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-sanitized variant (AddressSanitizer and UndefinedBehaviorSanitizer on
+# the host code only: argument validation and the block-sparse planner; the
+# device code is built as usual). For tests on the CPU; never installed.
+SAN_DIR = os.path.join(BUILD, "host_sanitized")
+SAN_LIB = os.path.join(SAN_DIR, "libfa_host_sanitized.so")
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+                 "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (it also holds
+    the UndefinedBehaviorSanitizer handlers)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("amdclang") or "/opt/rocm/llvm/bin/clang"
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True).stdout.strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise RuntimeError("the compiler's shared AddressSanitizer runtime was not found")
+    return out
+
+
+def build_host_sanitized() -> str:
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = sources()
+
+    def one(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *HOST_SANITIZE, "-c", src, "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    rt = asan_runtime()
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", SAN_LIB, *objs, rt,
+           f"-Wl,-rpath,{os.path.dirname(rt)}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if sys.argv[1:] == ["--host-sanitized"]:
+        print(build_host_sanitized())
+    else:
+        print(build(verbose=True))

@@ -39,13 +39,23 @@ class FaError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """Load libfa.so from the package directory (raises if it is not built)."""
+    """Load libfa.so from the package directory (raises if it is not built).
+    FA_LIBRARY in the environment names another build of the same sources
+    to load instead (the host-sanitized one, for the tests)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB):
-        raise RuntimeError(f"{LIB} is missing: build it with `python -m exact_io_aware_07_amd.build`")
-    L = ctypes.CDLL(LIB)
+    path = os.environ.get("FA_LIBRARY", LIB)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_07_amd.build`")
+    _lib = bind(ctypes.CDLL(path))
+    return _lib
+
+
+def bind(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the argument and result types of every entry point on a loaded
+    copy of the library (libfa.so, or a variant built from the same
+    sources)."""
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, i, i]
     L.fa_fwd.restype = i
@@ -104,7 +114,6 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_fp8_incoherent.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 
