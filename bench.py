@@ -93,15 +93,60 @@ def kernel_work(name: str, w) -> float:
 def traffic_for(name: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none for this kernel and workload or the kernel changed since."""
-    try:
-        with open(TRAFFIC_FILE) as fh:
-            rec = json.load(fh)["kernels"][name]
-    except (OSError, KeyError, ValueError):
-        return None
-    from exact_io_aware_07_amd.profiling import source_sha
-    if rec.get("workload") != workload or rec.get("source_sha256") != source_sha(name):
-        return None
-    return rec.get("fetch_bytes_per_launch", 0) + rec.get("write_bytes_per_launch", 0)
+    from exact_io_aware_07_amd.profiling import traffic_record
+    rec = traffic_record(TRAFFIC_FILE, workload, name)
+    return None if rec is None else rec[0] + rec[1]
+
+
+def kernel_rooflines(torch, w, iters: int = 10) -> dict:
+    """Each kernel of workload ``w``'s pass (the forward, and dQ and dK/dV
+    when it has a backward) launched back to back with two HIP events around
+    ``iters`` launches, on the launch stream, in batches until at least 50
+    launches and 100 ms; per kernel the median launch time, its algorithmic
+    work (kernel_work) over that time against the bf16 peak, and the HBM
+    traffic per launch from the committed counters (None when stale)."""
+    from exact_io_aware_07_amd import fa_bwd_dkdv, fa_bwd_dq, fa_fwd
+    inp = {n: (t.cuda() if t is not None else None) for n, t in W_make(w).items()}
+    q, k, v, do, kv = inp["q"], inp["k"], inp["v"], inp["do"], inp["kv_len"]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    dsum = torch.empty_like(lse)
+    stream = torch.cuda.current_stream()
+    fns = {"fwd": lambda: fa_fwd(q, k, v, o, lse, w.scale, w.causal, kv, stream)}
+    if w.backward:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        fns["dq"] = lambda: fa_bwd_dq(q, k, v, o, do, lse, dsum, dq, w.scale, w.causal, kv, stream)
+        fns["dkdv"] = lambda: fa_bwd_dkdv(q, k, v, do, lse, dsum, dk, dv, w.scale, w.causal, kv,
+                                          stream)
+    out = {}
+    for name, fn in fns.items():
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.3:
+            fn()
+            torch.cuda.synchronize()
+        batches, total = [], 0.0
+        while len(batches) * iters < 50 or total < 100.0:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(iters):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            batches.append(e0.elapsed_time(e1) / iters)
+            total += batches[-1] * iters
+        ms = statistics.median(batches)
+        work = kernel_work(name, w)
+        achieved = work / (ms * 1e-3)
+        out[name] = {"bound": BOUND[name], "avg_us": ms * 1e3, "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_FLOPS, "work_per_launch": work,
+                     "traffic": traffic_for(name, w.name)}
+    return out
+
+
+def W_make(w):
+    from exact_io_aware_07_amd import workloads as W
+    return W.make_inputs(w, seed=0)
 
 
 def run_gpu(args):
@@ -439,9 +484,11 @@ def extra_configs(torch, W, iters: int = 10):
         if w.kv_len_range is not None:
             eff = 4.0 * w.H * w.N * w.d * float(inp["kv_len"].sum().item())
             entry["tflops_effective_kv_len"] = eff / (ms * 1e-3) / 1e12
+        del inp, o, lse
+        if w.N >= 4096:
+            entry["kernels"] = kernel_rooflines(torch, w)
         res[w.name] = entry
         log(f"[bench] extra {w.name}: {entry}")
-        del inp, o, lse
     return res
 
 

@@ -19,7 +19,8 @@ transcendental / LDS instructions per MFMA instruction. ``traffic`` turns two ``
 WRITE_SIZE, KiB per dispatch) into HBM bytes per launch, each counter scaled
 by what it reads for a plain device copy of known size, and records the hash
 of the kernel sources the counters were taken on, so a stale figure is
-never reported for a changed kernel.
+never reported for a changed kernel; the JSON file keeps one record per
+workload.
 """
 from __future__ import annotations
 
@@ -154,8 +155,8 @@ def traffic(args) -> None:
     fw = _copy_factor(args.copy_write, "WRITE_SIZE", args.copy_bytes)
     fetch = _counter_means(args.fetch, "FETCH_SIZE")
     write = _counter_means(args.write, "WRITE_SIZE")
-    out = {"workload": args.workload, "copy_bytes": args.copy_bytes,
-           "fetch_scale": ff, "write_scale": fw, "kernels": {}}
+    out = {"copy_bytes": args.copy_bytes, "fetch_scale": ff, "write_scale": fw, "cmd": args.cmd,
+           "kernels": {}}
     md = ["# HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",
           f"Workload: `{args.workload}`.", "", "Commands:", "", "```", args.cmd, "```", "",
           f"Scale factors from a plain {args.copy_bytes} B device copy (the copy reads and "
@@ -174,9 +175,32 @@ def traffic(args) -> None:
                                      "source_sha256": source_sha(short)}
     with open(args.out_md, "w") as fh:
         fh.write("\n".join(md) + "\n")
+    # one record per workload; records of other workloads are kept
+    try:
+        with open(args.out_json) as fh:
+            allrec = json.load(fh)
+        if "workloads" not in allrec:
+            allrec = {"workloads": {}}
+    except (OSError, ValueError):
+        allrec = {"workloads": {}}
+    allrec["workloads"][args.workload] = out
     with open(args.out_json, "w") as fh:
-        json.dump(out, fh, indent=1)
+        json.dump(allrec, fh, indent=1, sort_keys=True)
         fh.write("\n")
+
+
+def traffic_record(path: str, workload: str, short: str):
+    """(fetch, write) bytes per launch of kernel ``short`` on ``workload`` from
+    a traffic file, or None when there is none or the kernel's source has
+    changed since the counters were taken."""
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)["workloads"][workload]["kernels"][short]
+    except (OSError, KeyError, ValueError, TypeError):
+        return None
+    if rec.get("source_sha256") != source_sha(short):
+        return None
+    return rec.get("fetch_bytes_per_launch", 0.0), rec.get("write_bytes_per_launch", 0.0)
 
 
 def main() -> None:
