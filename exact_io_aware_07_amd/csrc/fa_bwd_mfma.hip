@@ -129,6 +129,11 @@ template <int D>
 struct DkdvCfg {
   static constexpr int BQ = 64;                  // queries per tile
   static constexpr int MINW = (D == 128) ? 1 : 2;  // waves per SIMD the registers allow
+  // D = 64: the dP products of a sub-tile start from -D_i instead of 0, so
+  // that they yield dP - D directly, and a full tile forms S and dP of both
+  // sub-tiles before the exponentials of the first (measured faster at D =
+  // 64, slower at D = 128).
+  static constexpr bool DP_MINUS_D = (D == 64);
 };
 
 // SP: block-sparse, only the query tiles of the query blocks the block mask
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int kl = lane & 31;
   const int hh = lane >> 5;
 
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   };
   auto store_stats = [&](int p) {
     if (tid < BQ) lbuf(p)[tid] = (sreg == -INFINITY) ? 0.f : sreg * kLog2e;
-    else if (tid < 2 * BQ) dbuf(p)[tid - BQ] = sreg;
+    else if (tid < 2 * BQ) dbuf(p)[tid - BQ] = DkdvCfg<D>::DP_MINUS_D ? -sreg : sreg;
   };
   auto load_tiles = [&](int it, int p) {
     load_tile_lds<D, BQ, kBwdWaves>(rq, qbuf(p), it * BQ, wave, lane);
@@ -319,53 +324,90 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
     }
     const int q0 = tile_ix(c) * BQ;
     const bool live = FULL || ((key0 < kv_end) && (!a.causal || q0 + BQ - 1 >= key0));
+    // S = Q K^T and dP = dO V^T of query sub-tile qs (32 queries by this
+    // wave's 32 keys): lane = key; register r holds query qs*32 + 8(r/4) +
+    // 4hh + r%4.
+    auto sdp = [&](int qs, f32x16& s, f32x16& dp) {
+      const unsigned char* qt = qbuf(buf) + qs * (32 / L::RPI) * L::GB;
+      const unsigned char* gt = gbuf(buf) + qs * (32 / L::RPI) * L::GB;
+      s = f32x16{};
+      if constexpr (DkdvCfg<D>::DP_MINUS_D) {
+        // -D_i of each query, as stored in LDS
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 d4 = *(const f32x4*)&dbuf(buf)[qs * 32 + 8 * r4 + 4 * hh];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = d4[e];
+        }
+      } else {
+        dp = f32x16{};
+      }
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) s = Mfma<T>::mma32(*(const u32x4*)(qt + r_off[dc]), kf[dc], s);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) dp = Mfma<T>::mma32(*(const u32x4*)(gt + r_off[dc]), vf[dc], dp);
+    };
+    // In place: s becomes P = exp(S - LSE), dp becomes dS = P (dP - D).
+    auto probs = [&](int qs, f32x16& s, f32x16& dp, bool need_mask) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qi = qs * 32 + 8 * r4 + 4 * hh;
+        const f32x4 l4 = *(const f32x4*)&lbuf(buf)[qi];
+        const f32x4 d4 = *(const f32x4*)&dbuf(buf)[qi];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
+          if (need_mask) {
+            const int q = q0 + qi + e;
+            const bool vis = (my_key < kv_end) && (!a.causal || my_key <= q);
+            p = vis ? p : 0.f;
+          }
+          s[r] = p;
+          if constexpr (DkdvCfg<D>::DP_MINUS_D) dp[r] = p * dp[r];
+          else dp[r] = p * (dp[r] - d4[e]);
+        }
+      }
+    };
+    // dV^T += dO^T P^T and dK^T += Q^T dS^T over the sub-tile's 32 queries.
+    auto grads = [&](int qs, const f32x16& s, const f32x16& dp) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const u32x4 pf = pack8<T>(s, 8 * c2);
+        const u32x4 sf = pack8<T>(dp, 8 * c2);
+        const int rb = (2 * qs + c2) * L::rows16();
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const unsigned char* gp = gbuf(buf) + rb + t_off[dt];
+          const u32x2 g0 = lds_read_tr(gp), g1 = lds_read_tr(gp + L::half_step());
+          dv[dt] = Mfma<T>::mma32(u32x4{g0.x, g0.y, g1.x, g1.y}, pf, dv[dt]);
+          const unsigned char* qp = qbuf(buf) + rb + t_off[dt];
+          const u32x2 q0v = lds_read_tr(qp), q1v = lds_read_tr(qp + L::half_step());
+          dk[dt] = Mfma<T>::mma32(u32x4{q0v.x, q0v.y, q1v.x, q1v.y}, sf, dk[dt]);
+        }
+      }
+    };
     if (live) {
       // Full tiles: let the scheduler interleave the four MFMA chains with
       // the exponentials and LDS reads (iglp_opt strategy 0).
       if constexpr (FULL) __builtin_amdgcn_iglp_opt(0);
       const bool need_mask = !FULL && ((key0 + 32 > kv_end) || (a.causal && key0 + 31 > q0));
+      if constexpr (FULL && DkdvCfg<D>::DP_MINUS_D) {
+        f32x16 s[QS], dp[QS];
 #pragma unroll
-      for (int qs = 0; qs < QS; ++qs) {
-        const unsigned char* qt = qbuf(buf) + qs * (32 / L::RPI) * L::GB;
-        const unsigned char* gt = gbuf(buf) + qs * (32 / L::RPI) * L::GB;
-        f32x16 s = f32x16{}, dp = f32x16{};
+        for (int qs = 0; qs < QS; ++qs) sdp(qs, s[qs], dp[qs]);
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) s = Mfma<T>::mma32(*(const u32x4*)(qt + r_off[dc]), kf[dc], s);
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) dp = Mfma<T>::mma32(*(const u32x4*)(gt + r_off[dc]), vf[dc], dp);
-        // lane = key; register r holds query qs*32 + 8(r/4) + 4hh + r%4
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int qi = qs * 32 + 8 * r4 + 4 * hh;
-          const f32x4 l4 = *(const f32x4*)&lbuf(buf)[qi];
-          const f32x4 d4 = *(const f32x4*)&dbuf(buf)[qi];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
-            if (need_mask) {
-              const int q = q0 + qi + e;
-              const bool vis = (my_key < kv_end) && (!a.causal || my_key <= q);
-              p = vis ? p : 0.f;
-            }
-            s[r] = p;
-            dp[r] = p * (dp[r] - d4[e]);
-          }
+        for (int qs = 0; qs < QS; ++qs) {
+          probs(qs, s[qs], dp[qs], false);
+          grads(qs, s[qs], dp[qs]);
         }
+      } else {
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const u32x4 pf = pack8<T>(s, 8 * c2);
-          const u32x4 sf = pack8<T>(dp, 8 * c2);
-          const int rb = (2 * qs + c2) * L::rows16();
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const unsigned char* gp = gbuf(buf) + rb + t_off[dt];
-            const u32x2 g0 = lds_read_tr(gp), g1 = lds_read_tr(gp + L::half_step());
-            dv[dt] = Mfma<T>::mma32(u32x4{g0.x, g0.y, g1.x, g1.y}, pf, dv[dt]);
-            const unsigned char* qp = qbuf(buf) + rb + t_off[dt];
-            const u32x2 q0v = lds_read_tr(qp), q1v = lds_read_tr(qp + L::half_step());
-            dk[dt] = Mfma<T>::mma32(u32x4{q0v.x, q0v.y, q1v.x, q1v.y}, sf, dk[dt]);
-          }
+        for (int qs = 0; qs < QS; ++qs) {
+          f32x16 s, dp;
+          sdp(qs, s, dp);
+          probs(qs, s, dp, need_mask);
+          grads(qs, s, dp);
         }
       }
     }
@@ -497,7 +539,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int ql = lane & 31;
   const int hh = lane >> 5;
 

@@ -43,7 +43,7 @@ __device__ inline float clamp448(float x) { return fminf(fmaxf(x, -kE4m3Max), kE
 __device__ inline float block_max(float m, float* red) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
   if ((threadIdx.x & 63) == 0) red[wave] = m;
   __syncthreads();
   float r = red[0];
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256, Fp8Cfg<D>::OCC) void fwd_fp8_kernel(Fp8FwdArgs
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int ql = lane & 31;
   const int hh = lane >> 5;
 

@@ -468,7 +468,7 @@ __device__ inline int list_mask_blocks(const unsigned char* __restrict__ m, long
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   int base = 0;
   for (int c0 = lo; c0 < hi; c0 += NT) {
     const int blk = c0 + tid;
