@@ -610,6 +610,21 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
     qf[dc] = buf_load16(rq, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
     gf[dc] = buf_load16(rg, (uint32_t)(my_q * D + dc * 16 + hh * 8) * 2);
   }
+  auto load_k = [&](int j, int p) {
+    load_tile_lds<D, BC, kBwdWaves>(rk, kbuf(p), tile_ix(j) * BC, wave, lane);
+  };
+  auto load_v = [&](int j, int p) {
+    load_tile_lds<D, BC, kBwdWaves>(rv, vbuf(p), tile_ix(j) * BC, wave, lane);
+  };
+  // The first K/V tile and this row's LSE are fetched now, so that their
+  // latency overlaps the loads of O below (issued after the store of D, the
+  // copies would wait for it: the compiler keeps memory operations in order
+  // around a store it cannot tell apart).
+  if (ntiles > 0) {
+    load_k(0, 0);
+    load_v(0, 0);
+  }
+  const float l_raw = (my_q < N) ? a.lse[(size_t)bh * N + my_q] : 0.f;
   // D_i = sum_c dO_ic O_ic for this lane's row, from the dO fragments
   // already in VGPRs and the matching O fragments (this half of the wave
   // holds half of the row; the halves are summed). Written to the workspace
@@ -645,8 +660,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
   const bool single = (w_tiles == 1) && whole_row && n_full <= 0;
   float lse2 = 0.f;
   if (my_q < N) {
-    const float l = a.lse[(size_t)bh * N + my_q];
-    lse2 = (l == -INFINITY) ? 0.f : l * kLog2e;
+    lse2 = (l_raw == -INFINITY) ? 0.f : l_raw * kLog2e;
     // every piece of a row forms the same D_i; the first one stores it
     if (hh == 0 && piece0 == 0 && !single) a.dsum[(size_t)bh * N + my_q] = dsum;
   }
@@ -663,12 +677,6 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  auto load_k = [&](int j, int p) {
-    load_tile_lds<D, BC, kBwdWaves>(rk, kbuf(p), tile_ix(j) * BC, wave, lane);
-  };
-  auto load_v = [&](int j, int p) {
-    load_tile_lds<D, BC, kBwdWaves>(rv, vbuf(p), tile_ix(j) * BC, wave, lane);
-  };
   auto compute_sdp = [&](int p, f32x16 (&s)[KT], f32x16 (&dp)[KT]) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -683,11 +691,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
     }
   };
 
-  if (ntiles > 0) {
-    load_k(0, 0);
-    load_v(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-  }
+  if (ntiles > 0) __builtin_amdgcn_s_waitcnt(0);
   // Waves whose rows see one tile: D_i = sum_j P_ij dP_ij over that tile
   // (see `single`), from the same S and dP the tile pass recomputes bit for
   // bit. Only workgroups of at most two tiles can hold such a wave, so the
