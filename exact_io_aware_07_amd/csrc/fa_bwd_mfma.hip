@@ -134,6 +134,13 @@ struct DkdvCfg {
   // sub-tiles before the exponentials of the first (measured faster at D =
   // 64, slower at D = 128).
   static constexpr bool DP_MINUS_D = (D == 64);
+  // D = 64: the query tiles are walked from the last down to the first, so
+  // that the key blocks of a head running at the same time read the same Q
+  // and dO tile at about the same time and all but the first find it in L2
+  // (walked upwards, each key block starts at its own causal diagonal).
+  // Measured 3% faster on the GPT-2 shape; at D = 128 the compiler then
+  // schedules the LDS reads of the full tiles one product ahead (38% slower).
+  static constexpr bool DOWN = (D == 64);
 };
 
 // SP: block-sparse, only the query tiles of the query blocks the block mask
@@ -293,11 +300,14 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
     load_tile_lds<D, BQ, kBwdWaves>(rg, gbuf(p), it * BQ, wave, lane);
   };
 
+  // First tile of the walk and its buffer parity.
+  constexpr bool DOWN = DkdvCfg<D>::DOWN;
   auto prologue = [&]() {
     if (c_begin < c_end) {
-      load_tiles(tile_ix(c_begin), c_begin & 1);
-      load_stats(tile_ix(c_begin));
-      store_stats(c_begin & 1);
+      const int c0 = DOWN ? c_end - 1 : c_begin;
+      load_tiles(tile_ix(c0), DOWN ? 0 : c_begin & 1);
+      load_stats(tile_ix(c0));
+      store_stats(DOWN ? 0 : c_begin & 1);
     }
     // Unconditional, so that on every path into the loops below the K and
     // V fragment loads above are known complete: the compiler places waits
@@ -313,12 +323,12 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
   // meets a zero dO row and their dS is zero.
   auto tile = [&](int c, auto full, int buf) {
     constexpr bool FULL = decltype(full)::value;
-    // Tile c has landed everywhere; every wave is done with tile c-1, so
-    // the other buffers are free for tile c+1.
+    // Tile c has landed everywhere; every wave is done with the tile before
+    // it in the walk, so the other buffers are free for the one after.
     __syncthreads();
-    const bool more = c + 1 < c_end;
+    const bool more = DOWN ? c > c_begin : c + 1 < c_end;
     if (more) {
-      const int nxt = tile_ix(c + 1);
+      const int nxt = tile_ix(DOWN ? c - 1 : c + 1);
       load_tiles(nxt, buf ^ 1);
       load_stats(nxt);
     }
@@ -430,15 +440,29 @@ __global__ __launch_bounds__(kBwdThreads, DkdvCfg<D>::MINW) void dkdv_kernel(Bwd
     // this head's first tile is copied into the buffers.
     if (g > g0) __syncthreads();
     prologue();
-    int c = c_begin;
-    for (; c < c_full; ++c) tile(c, Part{}, c & 1);
-    // Full tiles in pairs of known parity (an odd first tile on its own).
-    if (c < c_end && (c & 1)) tile(c++, Full{}, 1);
-    for (; c + 1 < c_end; c += 2) {
-      tile(c, Full{}, 0);
-      tile(c + 1, Full{}, 1);
+    if constexpr (DOWN) {
+      // Step k runs tile c_end - 1 - k in the buffers of parity k & 1: the
+      // full tiles first, in pairs of known parity, then the partial ones
+      // (the causal diagonal, keys past kv_end).
+      const int n_full = c_end - max(c_full, c_begin);
+      int k = 0;
+      for (; k + 1 < n_full; k += 2) {
+        tile(c_end - 1 - k, Full{}, 0);
+        tile(c_end - 2 - k, Full{}, 1);
+      }
+      if (k < n_full) tile(c_end - 1 - k++, Full{}, 0);
+      for (; k < c_end - c_begin; ++k) tile(c_end - 1 - k, Part{}, k & 1);
+    } else {
+      int c = c_begin;
+      for (; c < c_full; ++c) tile(c, Part{}, c & 1);
+      // Full tiles in pairs of known parity (an odd first tile on its own).
+      if (c < c_end && (c & 1)) tile(c++, Full{}, 1);
+      for (; c + 1 < c_end; c += 2) {
+        tile(c, Full{}, 0);
+        tile(c + 1, Full{}, 1);
+      }
+      if (c < c_end) tile(c, Full{}, 0);
     }
-    if (c < c_end) tile(c, Full{}, 0);
   }
 
   // dK^T / dV^T accumulators: lane = key, registers = d in runs of 4.
