@@ -110,10 +110,10 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
   const bool by_items = SP && a.sp_items != nullptr;
   if (by_items) {
     const int* it4 = a.sp_items + 4 * (size_t)blockIdx.x;
-    bh = it4[0];
-    qb = it4[1];
-    piece0 = it4[2];
-    slot = it4[3];
+    bh = __builtin_amdgcn_readfirstlane(it4[0]);
+    qb = __builtin_amdgcn_readfirstlane(it4[1]);
+    piece0 = __builtin_amdgcn_readfirstlane(it4[2]);
+    slot = __builtin_amdgcn_readfirstlane(it4[3]);
   }
   const int b = bh / a.H;
 

@@ -479,7 +479,8 @@ __device__ inline int list_mask_blocks(const unsigned char* __restrict__ m, long
     int off = base, tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const int c = wcount[w];
+      // the same LDS word in every lane: uniform, so kept in an SGPR
+      const int c = __builtin_amdgcn_readfirstlane(wcount[w]);
       off += (w < wave) ? c : 0;
       tot += c;
     }
@@ -495,15 +496,20 @@ __device__ inline int list_mask_blocks(const unsigned char* __restrict__ m, long
 
 // Tiles of a listed sequence (block b holds tiles 2b and 2b + 1) whose
 // index is below lim: the sequence position of the first tile at or past
-// lim. The list is increasing, so a binary search; the same in every lane.
+// lim. The list is increasing, so a binary search. n and lim are the same
+// in every lane, so every lane reads the same entries: the entries pass
+// through readfirstlane, and the search runs on scalar registers and
+// branches (read from LDS, they would look divergent to the compiler, and
+// so would every loop bound derived from the result).
 __device__ inline int mask_tiles_below(const unsigned short* list, int n, int lim) {
   int lo = 0, hi = n;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (2 * (int)list[mid] < lim) lo = mid + 1;
+    if (2 * __builtin_amdgcn_readfirstlane((int)list[mid]) < lim) lo = mid + 1;
     else hi = mid;
   }
-  return 2 * lo - ((lo > 0 && 2 * (int)list[lo - 1] + 1 >= lim) ? 1 : 0);
+  const int last = lo > 0 ? __builtin_amdgcn_readfirstlane((int)list[lo - 1]) : 0;
+  return 2 * lo - ((lo > 0 && 2 * last + 1 >= lim) ? 1 : 0);
 }
 
 // Tile index of sequence position t (wave-uniform, in an SGPR).
