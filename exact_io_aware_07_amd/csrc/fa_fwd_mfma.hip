@@ -358,6 +358,16 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
     if (hh == 0)
       a.sp_part[(size_t)a.sp_nslots * kMaskBlock * D + (size_t)slot * kMaskBlock + r] =
           (l_tot > 0.f) ? m_ref * a.scale + fast_log2(l_tot) * kLn2 : -INFINITY;
+  } else if (!OUT_F32 && !GEN) {
+    // O of the wave's 32 rows through LDS (every wave is past its last
+    // tile, so the K and V buffers are free) and out in whole rows.
+    unsigned char* stage = wave == 0 ? Ks0 : wave == 1 ? Ks1 : wave == 2 ? Vs0 : Vs1;
+    __syncthreads();
+    stage_put<T, D>(stage, oacc, inv, lane);
+    __syncthreads();
+    stage_rows_out<D>(stage, (uint16_t*)a.o + head_off + (size_t)wq0 * D, N - wq0, lane);
+    if (hh == 0 && my_q < N)
+      a.lse[(size_t)bh * N + my_q] = (l_tot > 0.f) ? m_ref * a.scale + fast_log2(l_tot) * kLn2 : -INFINITY;
   } else if (my_q < N) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {

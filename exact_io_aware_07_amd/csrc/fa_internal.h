@@ -338,7 +338,12 @@ struct TileLayout {
 // holds 8 bytes of a row per register group; storing those directly leaves
 // each 128-byte line written in 16-byte parts by 8 separate instructions.
 // Where L2 evicts lines half-written (the dK/dV stage, which streams Q and
-// dO past), those lines are written back more than once.
+// dO past), those lines are written back more than once. The whole-row
+// stores are non-temporal: the lines go on to memory rather than staying
+// dirty in L2 until the kernel ends, where writing them back delays the
+// next kernel's start (by 1-3 us per kernel boundary in the GPT-2-shaped
+// step). Non-temporal stores of partial lines, straight from the
+// accumulators, made the kernels much slower instead.
 //
 // stage_put: a wave's 32 x D accumulator tile (lane l: row l % 32, elements
 // dt * 32 + 8 * r4 + 4 * (l / 32) + [0, 4) in acc[dt][4 * r4 + 0..3]), times
@@ -376,7 +381,7 @@ __device__ inline void stage_rows_out(const unsigned char* stage, uint16_t* dst,
   for (int i = 0; i < 32 / RPS; ++i) {
     const int row = i * RPS + cr;
     const u32x4 x = *(const u32x4*)(stage + L::off(row, cc));
-    if (row < n) *(u32x4*)(dst + (size_t)row * D + cc * 8) = x;
+    if (row < n) __builtin_nontemporal_store(x, (u32x4*)(dst + (size_t)row * D + cc * 8));
   }
 }
 
