@@ -274,10 +274,12 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
     // d = 64 also raise this wave's issue priority while it runs, so the
     // SIMD's other waves fill the gaps rather than the other way round; at
     // d = 128 (two waves per SIMD) the raise measured 3% slower on causal
-    // shapes and neutral on the others.
+    // shapes and neutral on the others. The raise comes first: s_setprio
+    // ends a scheduling region, so placed after iglp_opt it left the hint
+    // an empty region and the main block the default schedule.
     if constexpr (FULL) {
-      __builtin_amdgcn_iglp_opt(0);
       if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_iglp_opt(0);
     }
     if (FULL || j + 1 < w_tiles) compute_s(kbuf(par ^ 1), s_nxt);
 
