@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
   float m_ref = -INFINITY;  // running max of raw scores (both halves agree)
+  float mref2 = 0.f;        // m_ref * scale * log2(e), 0 while m_ref is -inf
   float l_run = 0.f;        // running sum over this half's keys, against m_ref
   const float sl2 = a.scale * kLog2e;
 
@@ -261,12 +262,13 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
       }
       mx = halves_max(mx);
       if (__any(mx > m_ref)) {
-        const float m_new = fmaxf(m_ref, mx);
+        const float m_new = max_nn(m_ref, mx);
         const float alpha = (m_new == m_ref) ? 1.f : fast_exp2((m_ref - m_new) * sl2);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         m_ref = m_new;
+        mref2 = (m_new == -INFINITY) ? 0.f : m_new * sl2;
       }
 
       // Main block of a full tile: ask the scheduler to interleave the MFMA
@@ -283,7 +285,6 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
     }
     if (FULL || j + 1 < w_tiles) compute_s(kbuf(par ^ 1), s_nxt);
 
-      const float mref2 = (m_ref == -INFINITY) ? 0.f : m_ref * sl2;
       float lsum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {

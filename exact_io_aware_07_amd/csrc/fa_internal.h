@@ -256,10 +256,20 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 // returns, in lanes 0-31, (own, lane + 32) and in lanes 32-63
 // (lane - 32, own), so max / sum of the pair is the two-lane result in
 // every lane.
+// max of two floats that are never NaN (scores, -inf for hidden keys, and
+// running maxima of those) as a single v_max_f32. fmaxf first quiets each
+// operand the compiler cannot prove canonical (a v_max_f32 of the value with
+// itself), two extra VALU instructions per call on these operands.
+__device__ inline float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ inline float halves_max(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  return max_nn(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 __device__ inline float halves_sum(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
