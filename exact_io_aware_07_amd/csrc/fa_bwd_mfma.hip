@@ -711,13 +711,20 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  auto compute_sdp = [&](int p, f32x16 (&s)[KT], f32x16 (&dp)[KT]) {
+  // d = 64: the dP products start from -D_i (dp0) instead of 0, so they
+  // yield dP - D and dS = P (dP - D) is one multiply: 64 fewer VALU
+  // instructions per two tiles. At d = 128 the same start made the compiler
+  // wait for each LDS read before its product, so there D is subtracted
+  // after the chain.
+  constexpr bool kDqDpMinusD = D == 64;
+  auto compute_sdp = [&](int p, f32x16 (&s)[KT], f32x16 (&dp)[KT], float dp0) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const unsigned char* kp = kbuf(p) + kt * (32 / L::RPI) * L::GB;
       const unsigned char* vp = vbuf(p) + kt * (32 / L::RPI) * L::GB;
       s[kt] = f32x16{};
-      dp[kt] = f32x16{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[kt][r] = kDqDpMinusD ? dp0 : 0.f;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) s[kt] = Mfma<T>::mma32(*(const u32x4*)(kp + r_off[dc]), qf[dc], s[kt]);
 #pragma unroll
@@ -734,7 +741,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
     __syncthreads();
     if (single) {
       f32x16 s0[KT], dp0[KT];
-      compute_sdp(0, s0, dp0);
+      compute_sdp(0, s0, dp0, 0.f);
       const int t0 = tile_ix(0) * BC;
       float acc = 0.f;
 #pragma unroll
@@ -769,7 +776,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
       // (iglp_opt strategy 2), measured 2% faster there and slower at 128.
       if constexpr (FULL && D == 64) __builtin_amdgcn_iglp_opt(2);
       f32x16 s_cur[KT], p_cur[KT];
-      compute_sdp(par, s_cur, p_cur);
+      compute_sdp(par, s_cur, p_cur, -dsum);
       const int t0 = tile_ix(j) * BC;
       const bool need_mask = !FULL && ((t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0));
 #pragma unroll
@@ -781,7 +788,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
             const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
             p = (key < kv_end && (!a.causal || key <= my_q)) ? p : 0.f;
           }
-          p_cur[kt][r] = p * (p_cur[kt][r] - dsum);
+          p_cur[kt][r] = kDqDpMinusD ? p * p_cur[kt][r] : p * (p_cur[kt][r] - dsum);
         }
       }
 #pragma unroll
