@@ -711,12 +711,9 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) t_off[dt] = L::tr_off(lane, dt * 32);
 
-  // d = 64: the dP products start from -D_i (dp0) instead of 0, so they
-  // yield dP - D and dS = P (dP - D) is one multiply: 64 fewer VALU
-  // instructions per two tiles. At d = 128 the same start made the compiler
-  // wait for each LDS read before its product, so there D is subtracted
-  // after the chain.
-  constexpr bool kDqDpMinusD = D == 64;
+  // The dP products start from -D_i (dp0) instead of 0, so they yield
+  // dP - D and dS = P (dP - D) is one multiply per element: 64 fewer VALU
+  // instructions per two full tiles.
   auto compute_sdp = [&](int p, f32x16 (&s)[KT], f32x16 (&dp)[KT], float dp0) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -724,7 +721,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
       const unsigned char* vp = vbuf(p) + kt * (32 / L::RPI) * L::GB;
       s[kt] = f32x16{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[kt][r] = kDqDpMinusD ? dp0 : 0.f;
+      for (int r = 0; r < 16; ++r) dp[kt][r] = dp0;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) s[kt] = Mfma<T>::mma32(*(const u32x4*)(kp + r_off[dc]), qf[dc], s[kt]);
 #pragma unroll
@@ -772,9 +769,13 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
       // Full tiles: raise this wave's issue priority while it runs its MFMA
       // chains, so the SIMD's other waves fill the gaps around them.
       if constexpr (FULL) __builtin_amdgcn_s_setprio(1);
-      // d = 64 full tiles: the compiler's exponential-interleave schedule
-      // (iglp_opt strategy 2), measured 2% faster there and slower at 128.
+      // Full tiles: the compiler's interleave schedules, exponential
+      // interleave (strategy 2) at d = 64 and strategy 1 at d = 128. With the
+      // -D start of the dP chains these keep the LDS reads ahead of the
+      // products; at d = 128 the default schedule then waited for each read
+      // before its product.
       if constexpr (FULL && D == 64) __builtin_amdgcn_iglp_opt(2);
+      if constexpr (FULL && D == 128) __builtin_amdgcn_iglp_opt(1);
       f32x16 s_cur[KT], p_cur[KT];
       compute_sdp(par, s_cur, p_cur, -dsum);
       const int t0 = tile_ix(j) * BC;
@@ -788,7 +789,7 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
             const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
             p = (key < kv_end && (!a.causal || key <= my_q)) ? p : 0.f;
           }
-          p_cur[kt][r] = kDqDpMinusD ? p * p_cur[kt][r] : p * (p_cur[kt][r] - dsum);
+          p_cur[kt][r] = p * p_cur[kt][r];
         }
       }
 #pragma unroll

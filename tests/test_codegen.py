@@ -84,7 +84,7 @@ CASES = [
     ("fa_bwd_mfma.hip", "dkdv_kernelINS_4BF16ELi128ELb0E", 64, 6.0, 4),
     ("fa_bwd_mfma.hip", "dkdv_kernelINS_4BF16ELi64ELb0E", 32, 3.0, 4),
     ("fa_bwd_mfma.hip", "dkdv_kernelINS_4BF16ELi128ELb1E", 64, 6.0, 4),
-    ("fa_bwd_mfma.hip", "dq_kernelINS_4BF16ELi128ELb0E", 96, 1.0, 20),
+    ("fa_bwd_mfma.hip", "dq_kernelINS_4BF16ELi128ELb0E", 96, 1.0, 32),
     ("fa_bwd_mfma.hip", "dq_kernelINS_4BF16ELi64ELb0E", 48, 1.0, 20),
     ("fa_fwd_mfma.hip", "fwd_mfma_kernelINS_4BF16ELi128ELb0ELb0ELb0E", 32, 6.0, 4),
     ("fa_fwd_mfma.hip", "fwd_mfma_kernelINS_4BF16ELi128ELb1ELb0ELb0E", 32, 6.0, 4),
