@@ -251,11 +251,6 @@ struct Mfma<F16> {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Reductions across the two halves of a wave (lane l with lane l ^ 32) on
-// v_permlane32_swap, a VALU op with no LDS round trip: called with (x, x) it
-// returns, in lanes 0-31, (own, lane + 32) and in lanes 32-63
-// (lane - 32, own), so max / sum of the pair is the two-lane result in
-// every lane.
 // max of two floats that are never NaN (scores, -inf for hidden keys, and
 // running maxima of those) as a single v_max_f32. fmaxf first quiets each
 // operand the compiler cannot prove canonical (a v_max_f32 of the value with
@@ -266,6 +261,11 @@ __device__ inline float max_nn(float a, float b) {
   return r;
 }
 
+// Reductions across the two halves of a wave (lane l with lane l ^ 32) on
+// v_permlane32_swap, a VALU op with no LDS round trip: called with (x, x) it
+// returns, in lanes 0-31, (own, lane + 32) and in lanes 32-63
+// (lane - 32, own), so max / sum of the pair is the two-lane result in
+// every lane.
 __device__ inline float halves_max(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
