@@ -780,15 +780,18 @@ __global__ __launch_bounds__(kBwdThreads, DqCfg<D>::MINW) void dq_kernel(BwdArgs
       compute_sdp(par, s_cur, p_cur, -dsum);
       const int t0 = tile_ix(j) * BC;
       const bool need_mask = !FULL && ((t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0));
+      // Value r of sub-tile kt is key t0 + 4 hh + c with c = 32 kt + 8 (r / 4)
+      // + r % 4 a constant, visible iff the key is at most
+      // min(kv_end - 1, my_q): one compare with a per-lane bound per value.
+      int lim = kv_end - 1;
+      if (a.causal) lim = min(lim, my_q);
+      lim -= t0 + 4 * hh;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(fmaf(s_cur[kt][r], sl2, -lse2));
-          if (need_mask) {
-            const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            p = (key < kv_end && (!a.causal || key <= my_q)) ? p : 0.f;
-          }
+          if (need_mask) p = (kt * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? p : 0.f;
           p_cur[kt][r] = p * p_cur[kt][r];
         }
       }

@@ -242,14 +242,18 @@ __global__ __launch_bounds__(kThreads, FwdTile<D>::OCC) void fwd_mfma_kernel(Fwd
         const int t0 = tile_ix(j) * BC;
         const bool need_mask = (t0 + BC > kv_end) || (a.causal && t0 + BC - 1 > wq0 + delta);
         if (need_mask) {
+          // Score r of sub-tile kt is key t0 + 4 hh + c with c = 32 kt +
+          // 8 (r / 4) + r % 4 a constant, visible iff the key is at most
+          // min(kv_end - 1, my_q + delta): one compare of c with a per-lane
+          // bound per score.
+          int lim = kv_end - 1;
+          if (a.causal) lim = min(lim, my_q + delta);
+          lim -= t0 + 4 * hh;
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = t0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              const bool vis = key < kv_end && (!a.causal || key <= my_q + delta);
-              if (!vis) s_cur[kt][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+              if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s_cur[kt][r] = -INFINITY;
           }
         }
       }
